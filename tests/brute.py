@@ -1,0 +1,52 @@
+"""Scalar brute force of the attention core, in pure Python (``math`` only), for
+tiny shapes.  Written independently of ``oracle/`` (no shared code): loops over
+every token, head, key and dimension, straight from the definitions -- RMSNorm
+per head row with eps inside the root, rotate-half RoPE with frequency
+theta^(-2i/d), scores scaled by 1/sqrt(d), causal softmax, weighted sum of V,
+query head t reading KV head floor(t / g)."""
+
+import math
+
+
+def _norm_row(row, gamma, eps):
+    ms = sum(x * x for x in row) / len(row)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [row[i] * r * gamma[i] for i in range(len(row))]
+
+
+def _rope_row(row, pos, theta):
+    d = len(row)
+    h = d // 2
+    out = [0.0] * d
+    for i in range(h):
+        ang = pos * theta ** (-(2.0 * i) / d)
+        c, s = math.cos(ang), math.sin(ang)
+        out[i] = row[i] * c - row[i + h] * s
+        out[i + h] = row[i + h] * c + row[i] * s
+    return out
+
+
+def prefill(q, k, v, q_gamma, k_gamma, lengths, n_q_heads, n_kv_heads, eps, theta):
+    """q[t][h][d], k/v[t][h][d] nested lists (packed tokens).  Returns o[t][h][d]."""
+    g = n_q_heads // n_kv_heads
+    d = len(q[0][0])
+    scale = 1.0 / math.sqrt(d)
+    out = []
+    base = 0
+    for L in lengths:
+        qh = [[_rope_row(_norm_row(q[base + i][t], q_gamma, eps), i, theta)
+               for t in range(n_q_heads)] for i in range(L)]
+        kh = [[_rope_row(_norm_row(k[base + j][u], k_gamma, eps), j, theta)
+               for u in range(n_kv_heads)] for j in range(L)]
+        for i in range(L):
+            row = []
+            for t in range(n_q_heads):
+                u = t // g
+                s = [sum(qh[i][t][e] * kh[j][u][e] for e in range(d)) * scale for j in range(i + 1)]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                z = sum(w)
+                row.append([sum(w[j] * v[base + j][u][e] for j in range(i + 1)) / z for e in range(d)])
+            out.append(row)
+        base += L
+    return out

@@ -1,0 +1,126 @@
+"""The oracle against its pins (CPU only)."""
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import attention as A
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_brute_force_full_head_dim():
+    pins.pin_brute_force(d=128)
+
+
+# ------------------------------------------------------------------ mutations
+# Each plants one plausible mistake in the oracle (on the CPU) and checks that
+# at least one pin fails, so the pins would have caught it.
+
+def _rope_sign_flip(x, positions, theta):
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * A.rope_inv_freq(x.shape[-1], theta)
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    return np.concatenate([x[..., :h] * c + x[..., h:] * s, x[..., h:] * c - x[..., :h] * s], -1)
+
+
+def _rope_interleaved(x, positions, theta):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * A.rope_inv_freq(d, theta)
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = a * c - b * s
+    y[..., 1::2] = b * c + a * s
+    return y
+
+
+def _rope_wrong_freq(head_dim, theta):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -i / head_dim)
+
+
+def _norm_eps_outside(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * gamma
+
+
+def _norm_all_heads(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=(-2, -1), keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+def _norm_no_gamma(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _kv_modulo(t, n_q_heads, n_kv_heads):
+    return t % n_kv_heads
+
+
+def _softmax_strict_mask(scores, q_pos, k_pos):
+    vis = np.asarray(k_pos)[None, :] < np.asarray(q_pos)[:, None]
+    vis[:, 0] = True
+    s = np.where(vis, scores, -np.inf)
+    e = np.where(vis, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def _softmax_no_mask(scores, q_pos, k_pos):
+    s = np.asarray(scores, dtype=np.float64)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+_orig_qk = A.qk_norm_rope
+
+
+def _order_swapped(x, gamma, positions, eps, theta, order="norm_rope"):
+    other = "rope_norm" if order == "norm_rope" else "norm_rope"
+    return _orig_qk(x, gamma, positions, eps, theta, other)
+
+
+_orig_attend = A._attend
+
+
+def _attend_wrong_scale(q_hat, k_hat, v, q_pos, k_pos, hq, hkv, scale, heads=None):
+    return _orig_attend(q_hat, k_hat, v, q_pos, k_pos, hq, hkv, scale * scale * 128 / 64 ** 0.5, heads)
+
+
+MUTATIONS = {
+    "rope_sign_flip": ("rope_rotate_half", _rope_sign_flip),
+    "rope_interleaved_pairs": ("rope_rotate_half", _rope_interleaved),
+    "rope_freq_missing_factor_2": ("rope_inv_freq", _rope_wrong_freq),
+    "norm_eps_outside_root": ("rms_norm_heads", _norm_eps_outside),
+    "norm_over_all_heads": ("rms_norm_heads", _norm_all_heads),
+    "norm_gamma_dropped": ("rms_norm_heads", _norm_no_gamma),
+    "gqa_modulo_map": ("kv_head_for_q_head", _kv_modulo),
+    "mask_off_by_one": ("causal_softmax", _softmax_strict_mask),
+    "mask_missing": ("causal_softmax", _softmax_no_mask),
+    "order_swapped": ("qk_norm_rope", _order_swapped),
+    "scale_wrong": ("_attend", _attend_wrong_scale),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(A, attr, fn)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    try:
+        pins.pin_brute_force(d=128)
+    except (AssertionError, ValueError):
+        failed.append("pin_brute_force_d128")
+    assert failed, f"no pin caught the planted mistake {name}"
