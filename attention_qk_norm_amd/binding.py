@@ -1,0 +1,216 @@
+"""ctypes binding of libqwattn (argument marshalling only: every step of the
+path runs in the library's HIP kernels).  The names follow the C entry points
+declared in include/qwattn.h.
+
+Tensors are torch tensors on the current HIP device; the call is enqueued on
+``torch.cuda.current_stream()``.  The library is loaded on first use and a
+missing build raises, so nothing falls back to another implementation."""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libqwattn.so")
+_lib = None
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = range(6)
+F32, BF16 = 0, 1
+HEAD_DIM = 128
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+                ("order", ctypes.c_int32)]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("stride_seq", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("stride_tok", ctypes.c_int64),
+                ("capacity", ctypes.c_int32)]
+
+
+class QwattnError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"libqwattn status {status}: {detail}")
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load(path=None):
+    """Load libqwattn.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libqwattn is not built ({p} missing): run __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pp, pc = ctypes.POINTER(Params), ctypes.POINTER(CacheDesc)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.qwattn_qk_norm_rope.argtypes = [pp, i32, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+    lib.qwattn_qk_norm_rope.restype = i32
+    lib.qwattn_prefill.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, ip, i32, vp, vp, vp, pc, vp, sz, vp]
+    lib.qwattn_prefill.restype = i32
+    lib.qwattn_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, i32, vp, vp, sz, vp]
+    lib.qwattn_decode.restype = i32
+    lib.qwattn_prefill_workspace_size.argtypes = [pp, i32, i32, i64, i32, i32]
+    lib.qwattn_prefill_workspace_size.restype = sz
+    lib.qwattn_decode_workspace_size.argtypes = [pp, i32, i32, i64]
+    lib.qwattn_decode_workspace_size.restype = sz
+    lib.qwattn_status_str.argtypes = [i32]
+    lib.qwattn_status_str.restype = ctypes.c_char_p
+    lib.qwattn_last_error.argtypes = []
+    lib.qwattn_last_error.restype = ctypes.c_char_p
+    lib.qwattn_set_timing_events.argtypes = [vp, vp]
+    lib.qwattn_set_timing_events.restype = i32
+    lib.qwattn_abi_version.argtypes = []
+    lib.qwattn_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_params(n_q_heads, n_kv_heads, eps=1e-6, rope_theta=1e6, softmax_scale=0.0, head_dim=HEAD_DIM, order=0):
+    return Params(n_q_heads, n_kv_heads, head_dim, eps, rope_theta, softmax_scale, order)
+
+
+def _check(status):
+    if status != OK:
+        raise QwattnError(status, _lib.qwattn_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def cache_desc(k_cache):
+    """Descriptor of a [n_seq][n_kv_heads][capacity][128] cache tensor (strides may vary)."""
+    s = k_cache.stride()
+    return CacheDesc(s[0], s[1], s[2], k_cache.shape[2])
+
+
+def _check_cache_pair(k_cache, v_cache):
+    if v_cache is None or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share one shape and stride layout")
+    if k_cache.dim() != 4 or k_cache.shape[3] != HEAD_DIM or k_cache.stride(3) != 1:
+        raise ValueError("cache must be [n_seq][n_kv_heads][capacity][128] with the last dim contiguous")
+
+
+def qk_norm_rope(params, q, k, q_gamma, k_gamma, positions, q_out=None, k_out=None):
+    """QK-Norm then RoPE of q [n_tok, Hq, 128] and/or k [n_tok, Hkv, 128] at ``positions``."""
+    lib = load()
+    ref = q if q is not None else k
+    for t, n in ((q, "q"), (k, "k"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"), (positions, "positions")):
+        _dev(t, n)
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    n_tok = ref.shape[0]
+    _check(lib.qwattn_qk_norm_rope(ctypes.byref(params), _dtype_code(ref), _ptr(q), _ptr(k), _ptr(q_gamma),
+                                   _ptr(k_gamma), _ptr(positions), n_tok, _ptr(q_out), _ptr(k_out), _stream()))
+    return q_out, k_out
+
+
+def set_timing_events(begin, end):
+    """Raw hipEvent_t handles (ints) recorded around the next call's dominant kernel."""
+    _check(load().qwattn_set_timing_events(ctypes.c_void_p(begin) if begin else None,
+                                           ctypes.c_void_p(end) if end else None))
+
+
+def prefill_workspace_size(params, dtype_code, n_seq, n_tok, max_seqlen, with_cache):
+    return load().qwattn_prefill_workspace_size(ctypes.byref(params), dtype_code, n_seq, n_tok, max_seqlen,
+                                                1 if with_cache else 0)
+
+
+def decode_workspace_size(params, dtype_code, n_seq, total_start_pos):
+    return load().qwattn_decode_workspace_size(ctypes.byref(params), dtype_code, n_seq, total_start_pos)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def prefill(params, q, k, v, q_gamma, k_gamma, cu_seqlens, cu_seqlens_host=None, out=None,
+            k_cache=None, v_cache=None, workspace=None):
+    """Causal GQA prefill over packed sequences.  ``cu_seqlens`` is a device
+    int32 tensor [n_seq + 1]; ``cu_seqlens_host`` the same values on the host
+    (a list, numpy array or CPU tensor; read from the device when omitted)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"),
+                 (cu_seqlens, "cu_seqlens")):
+        _dev(t, n)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu()
+    cu_h = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    n_seq = cu_h.numel() - 1
+    n_tok = int(cu_h[-1]) if n_seq > 0 else 0
+    max_len = int((cu_h[1:] - cu_h[:-1]).max()) if n_seq > 0 else 0
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    desc = None
+    if k_cache is not None:
+        _check_cache_pair(k_cache, v_cache)
+        desc = cache_desc(k_cache)
+    nbytes = prefill_workspace_size(params, dt, n_seq, n_tok, max_len, k_cache is not None)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib.qwattn_prefill(ctypes.byref(params), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(q_gamma), _ptr(k_gamma),
+                              ctypes.c_void_p(cu_seqlens.data_ptr()),
+                              cu_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
+                              _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc) if desc else None,
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def decode(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, start_pos_host=None, out=None,
+           workspace=None):
+    """One new token per sequence against the cache; appends k̂/v at start_pos."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"),
+                 (start_pos, "start_pos")):
+        _dev(t, n)
+    if start_pos_host is None:
+        start_pos_host = start_pos.cpu()
+    sp_h = torch.as_tensor(start_pos_host, dtype=torch.int32).contiguous()
+    n_seq = sp_h.numel()
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_cache_pair(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    nbytes = decode_workspace_size(params, dt, n_seq, int(sp_h.sum()))
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib.qwattn_decode(ctypes.byref(params), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(q_gamma), _ptr(k_gamma),
+                             _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                             ctypes.c_void_p(start_pos.data_ptr()),
+                             sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
+    return out

@@ -1,0 +1,62 @@
+"""Build libqwattn.so in-tree for gfx950 with hipcc.
+
+    python -m attention_qk_norm_amd.build        # or: __graft_entry__.build()
+
+Every source is compiled on each call (one process per file, in parallel),
+then linked into ``attention_qk_norm_amd/lib/libqwattn.so``.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libqwattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["qwattn_api.cpp", "k_normrope.hip", "k_prefill.hip", "k_attn_f32.hip", "k_decode.hip"]
+
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code (the host pass of
+# hipcc warns that it does not know the feature; that is harmless).
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _compile(src, objdir):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
+    return obj, r.returncode, "\n".join(msgs)
+
+
+def build(verbose=False):
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        results = list(ex.map(lambda s: _compile(s, objdir), SOURCES))
+    failed = False
+    for (obj, rc, msg), src in zip(results, SOURCES):
+        if msg.strip() and (verbose or rc):
+            print(f"--- {src}\n{msg}", file=sys.stderr)
+        failed |= rc != 0
+    if failed:
+        raise RuntimeError("libqwattn: compilation failed")
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _, _ in results]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError("libqwattn: link failed\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,254 @@
+// Split-K decode over a bf16 KV cache (HBM-bound).
+//
+// One new query token per sequence attends to the cache slots 0 .. start_pos[i]
+// of its KV head, the new key having been normed, rotated at start_pos and
+// appended by the prologue ("第 20 章 Qwen3 与 Qwen3.5" §20.3: only the new K is
+// rotated; cached keys already carry their rotation).  The key axis of every
+// (sequence, KV head) is cut into chunks; a workgroup streams one chunk, its four
+// waves taking interleaved 32-key blocks, and leaves a partial (m, l, acc[128])
+// per query head.  A second kernel merges the partials with the exact softmax
+// identity o = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
+//
+// Per 32-key block a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// (A = K rows loaded straight from HBM as 16-byte fragments, B = the g <= 16
+// query heads of the group, resident), so each lane owns one head column and
+// the softmax is lane-local plus two lane swaps.  The probabilities, rounded to
+// bf16, are the B operand of O^T = V^T P^T; V goes HBM -> registers -> the
+// wave's own LDS slot and comes back transposed through ds_read_b64_tr_b16.
+// Every K and V byte is read once, in 16-byte lane loads.
+#include "kernels.h"
+
+namespace qw {
+namespace {
+
+constexpr int kBlockKeys = 32;
+constexpr int kRowBytes = kD * 2;
+
+// V block in LDS: 32 rows x 256 B.  The transposed reads of one half-wave touch
+// 8 rows x 32 bytes; XOR-ing the 16-byte chunk with (row & 7) << 1 spreads those
+// 8 rows over the 8 32-byte windows of a 256-byte bank line.
+__device__ __forceinline__ int v_swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4);
+}
+
+__global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kBlockKeys * kRowBytes + 4 * 2 * 16 * 4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int u = blockIdx.x % a.Hkv;
+  const int cg = blockIdx.x / a.Hkv;
+  // sequence of this chunk: chunk_off[i] <= cg < chunk_off[i + 1]
+  int lo = 0, hi = a.n_seq;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a.chunk_off[mid + 1] <= cg) lo = mid + 1; else hi = mid;
+  }
+  const int i = lo;
+  if (i >= a.n_seq) return;
+  const int n_keys = a.start_pos[i] + 1;
+  const int kbeg = (cg - a.chunk_off[i]) * a.chunk;
+  const int kend = min(n_keys, kbeg + a.chunk);
+
+  const int hh = lane & 15, q4 = lane >> 4;  // head column, lane group
+  const bool hvalid = hh < a.g;
+
+  // query fragments: B[k = dim 32kk + 8q4 + e][n = head hh]
+  bf16x8 qf[4];
+  {
+    const uint16_t* src = a.qhat + ((int64_t)i * a.Hq + u * a.g + (hvalid ? hh : 0)) * kD + 8 * q4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 raw = hvalid ? *reinterpret_cast<const u32x4*>(src + 32 * kk) : u32x4{0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const uint16_t* kb = a.k_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
+  const uint16_t* vb = a.v_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
+  lds_u8* vs = (lds_u8*)(smem) + w * kBlockKeys * kRowBytes;
+
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // transposed-read coordinates: group q4 reads rows 4 q4 + (lam >> 2) (+16)
+  const int lam = lane & 15;
+  const int v_row = 4 * q4 + (lam >> 2);
+  const int v_col = 4 * (lam & 3);  // + 16 db, elements
+
+  for (int b0 = kbeg + w * kBlockKeys; b0 < kend; b0 += 4 * kBlockKeys) {
+    // K fragments: A[m = key b0 + 16 sb + hh][k = dim 32kk + 8 q4 + e]
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int key = b0 + 16 * sb + hh;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kr[sb][kk] = key < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * a.cs_tok + 32 * kk + 8 * q4)
+                                : u32x4{0, 0, 0, 0};
+    }
+    // V rows of the block: lane chunk c = lane + 64 m -> row c / 16, 16-byte chunk c % 16
+    u32x4 vr[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int c = lane + 64 * m;
+      const int key = b0 + (c >> 4);
+      vr[m] = key < kend ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * a.cs_tok + (c & 15) * 8)
+                         : u32x4{0, 0, 0, 0};
+    }
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[sb][kk]), qf[kk],
+                                                          sacc[sb], 0, 0, 0);
+    }
+    // stage V in this wave's LDS slot (only this wave reads it)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int c = lane + 64 * m;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vs + v_swz(c >> 4, c & 15)) = vr[m];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // softmax over the block: sacc[sb][j] = key b0 + 16sb + 4q4 + j of head hh
+    float sv[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = b0 + 16 * sb + 4 * q4 + j;
+        const float x = key < kend ? sacc[sb][j] * a.scale_log2e : -INFINITY;
+        sv[4 * sb + j] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
+      psum += p;
+      pf[e] = (__bf16)p;  // virtual key 8 q4 + e
+    }
+    l_run = l_run * alpha + psum;
+
+    // O^T[d][head] += V^T[d][keys] P^T[keys][head]
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int col = 16 * db + v_col;
+      const int off = (col & 7) * 2;
+      const bf16x8 va = concat_tr16(lds_read_tr16(vs + v_swz(v_row, col >> 3) + off),
+                                    lds_read_tr16(vs + v_swz(v_row + 16, col >> 3) + off));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[db][j] *= alpha;
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[db], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four waves: m is uniform over a head's lane groups; l is not
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  __syncthreads();
+  float* ob = reinterpret_cast<float*>(smem);           // [4 waves][16 heads][128 d]
+  float* ml = ob + 4 * 16 * kD;                          // [4 waves][2][16]
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ob[(w * 16 + hh) * kD + 16 * db + 4 * q4 + j] = o[db][j];
+  if (q4 == 0) {
+    ml[(w * 2 + 0) * 16 + hh] = m_run;
+    ml[(w * 2 + 1) * 16 + hh] = l_run;
+  }
+  __syncthreads();
+  for (int e = tid; e < a.g * kD; e += 256) {
+    const int h = e / kD, d = e % kD;
+    float M = -1e30f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, ml[(ww * 2) * 16 + h]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(ml[(ww * 2) * 16 + h] - M);
+      acc += f * ob[(ww * 16 + h) * kD + d];
+      lsum += f * ml[(ww * 2 + 1) * 16 + h];
+    }
+    float* dst = a.partial + ((int64_t)cg * a.Hq + u * a.g + h) * kPartStride;
+    dst[d] = acc;
+    if (d == 0) {
+      dst[kD] = M;
+      dst[kD + 1] = lsum;
+    }
+  }
+}
+
+// One wave per (sequence, query head): merge its chunks' partials.
+__global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
+  const int i = blockIdx.x / a.Hq, t = blockIdx.x % a.Hq;
+  const int lane = threadIdx.x;
+  const int c0 = a.chunk_off[i], c1 = a.chunk_off[i + 1];
+  float M = -1e30f;
+  for (int c = c0; c < c1; ++c) M = fmaxf(M, a.partial[((int64_t)c * a.Hq + t) * kPartStride + kD]);
+  float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const float* p = a.partial + ((int64_t)c * a.Hq + t) * kPartStride;
+    const float f = __builtin_amdgcn_exp2f(p[kD] - M);
+    lsum += f * p[kD + 1];
+    acc0 += f * p[2 * lane];
+    acc1 += f * p[2 * lane + 1];
+  }
+  const float inv = 1.0f / lsum;
+  *reinterpret_cast<uint32_t*>(a.out + ((int64_t)i * a.Hq + t) * kD + 2 * lane) = pack_bf16x2(acc0 * inv, acc1 * inv);
+}
+
+// chunk_off[i] = sum_{i' < i} ceil((start_pos[i'] + 1) / chunk); one workgroup.
+__global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* start_pos, int n_seq, int chunk,
+                                                      int32_t* chunk_off) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_seq + 1023) / 1024;
+  const int lo = min(n_seq, tid * per), hi = min(n_seq, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += (start_pos[i] + chunk) / chunk;
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < 1024; ++i) { const int v = part[i]; part[i] = acc; acc += v; }
+    chunk_off[n_seq] = acc;
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int i = lo; i < hi; ++i) { chunk_off[i] = acc; acc += (start_pos[i] + chunk) / chunk; }
+}
+
+}  // namespace
+
+hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int32_t* chunk_off,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, start_pos, n_seq, chunk, chunk_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, int total_chunks, hipStream_t st) {
+  if (total_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_decode_split, dim3((unsigned)((int64_t)total_chunks * a.Hkv)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
+  if (a.n_seq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)((int64_t)a.n_seq * a.Hq)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qw

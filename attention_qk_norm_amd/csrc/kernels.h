@@ -1,0 +1,98 @@
+// Kernel argument blocks and host-side launchers of libqwattn.  Launchers return
+// hipSuccess or the launch error; they do no validation (the C-ABI layer does).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qw {
+
+// ---------------------------------------------------------------- norm + RoPE
+// Row sources: tensor 0 = q (normed, rotated), 1 = k (normed, rotated),
+// 2 = v (copied unchanged into the cache).  heads[i] == 0 skips tensor i.
+enum NormRopeMode : int {
+  kPosExplicit = 0,  // token n at position pos[n]; outputs contiguous
+  kPosPacked = 1,    // token n in sequence s (from cu), position n - cu[s]
+  kPosDecode = 2,    // token n is sequence n's new token, at position pos[n]
+};
+
+struct NormRopeArgs {
+  const void* x[3];
+  void* out[2];             // contiguous q / k outputs (k unused when k_cache set)
+  const void* gamma[2];
+  int heads[3];
+  void* k_cache;            // when set, rotated k goes to cache(seq, head, pos)
+  void* v_cache;            // when set (and heads[2] > 0), v goes to cache(seq, head, pos)
+  int64_t cs_seq, cs_head, cs_tok;
+  const int32_t* pos;
+  const int32_t* cu;
+  int n_seq;
+  int mode;
+  int64_t n_tok;
+  float eps;
+  RopeFreq rope;
+};
+
+hipError_t launch_normrope(bool bf16, const NormRopeArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill
+// Work list of (sequence, query tile) pairs, heaviest first.
+struct PlanArgs {
+  const int32_t* cu;
+  int n_seq;
+  int bm_tok;        // query tokens per tile
+  int max_tiles;     // max over sequences of ceil(L / bm_tok)
+  int n_items;       // sum over sequences of ceil(L / bm_tok)
+  int32_t* scratch;  // 4 * (max_tiles + 1) + n_seq ints
+  int2* items;
+};
+hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
+
+struct PrefillArgs {
+  const void* q;            // raw [n_tok][Hq][128]
+  const void* q_gamma;
+  const void* qhat;         // fp32 path: normed+rotated q [n_tok][Hq][128] (fp32)
+  const void* khat;         // rotated keys; row (s, h, j) at khat + h*ks_head + base(s) + j*ks_tok
+  int64_t ks_seq, ks_head, ks_tok;
+  int k_packed;             // 1: base(s) = cu[s]*ks_tok; 0: base(s) = s*ks_seq
+  const void* v;            // V rows; row (s, h, j) at v + h*vs_head + base(s) + j*vs_tok
+  int64_t vs_seq, vs_head, vs_tok;
+  int v_packed;
+  const int32_t* cu;        // packed: sequence offsets; decode: unused
+  const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token
+  const int2* items;
+  void* out;
+  int n_seq, Hq, Hkv, g, bm_tok;
+  int decode;               // fp32 path: items are (seq, 0), one query token at start_pos
+  float scale_log2e;        // softmax scale * log2(e)
+  float eps;
+  RopeFreq rope;
+};
+constexpr int kPrefillRows = 128;  // query rows (g heads x bm_tok tokens) per workgroup
+constexpr int kAttnF32Rows = 64;   // fp32 path: query rows per workgroup
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st);
+hipError_t launch_attn_f32(const PrefillArgs& a, int n_items, hipStream_t st);
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+  const uint16_t* qhat;     // normed+rotated new queries [n_seq][Hq][128] (bf16)
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  int64_t cs_seq, cs_head, cs_tok;
+  const int32_t* start_pos; // keys of sequence i: slots 0 .. start_pos[i] (inclusive)
+  const int32_t* chunk_off; // [n_seq + 1] prefix of chunk counts
+  float* partial;           // [total_chunks][Hq][kPartStride]
+  uint16_t* out;            // [n_seq][Hq][128]
+  int n_seq, Hq, Hkv, g;
+  int chunk;                // keys per split (multiple of kDecodeKeysPerPass)
+  float scale_log2e;
+};
+constexpr int kPartStride = 132;   // 128 accumulators, m, l, 2 pad floats
+constexpr int kDecodeKeysPerPass = 128;  // 4 waves x 32 keys
+hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int32_t* chunk_off,
+                              hipStream_t st);
+hipError_t launch_decode_split(const DecodeArgs& a, int total_chunks, hipStream_t st);
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace qw

@@ -1,0 +1,475 @@
+// C-ABI of libqwattn: argument validation, planning, workspace layout and
+// launches.  Every check runs before the first HIP call, so an invalid call
+// enqueues nothing and writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/qwattn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_begin = nullptr, g_ev_end = nullptr;
+
+// Records the timing hook around one launch and clears it.
+template <class F>
+hipError_t timed_launch(hipStream_t st, F&& launch) {
+  hipEvent_t b = g_ev_begin, e = g_ev_end;
+  g_ev_begin = g_ev_end = nullptr;
+  hipError_t r;
+  if (b && (r = hipEventRecord(b, st)) != hipSuccess) return r;
+  if ((r = launch()) != hipSuccess) return r;
+  if (e && (r = hipEventRecord(e, st)) != hipSuccess) return r;
+  return hipSuccess;
+}
+
+qwattn_status fail(qwattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+qwattn_status hip_fail(hipError_t e, const char* what) {
+  return fail(QWATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int elem_bytes(qwattn_dtype dt) { return dt == QWATTN_BF16 ? 2 : 4; }
+
+qwattn_status check_params(const qwattn_params* p, qwattn_dtype dt) {
+  if (!p) return fail(QWATTN_ERR_INVALID_ARG, "params is NULL");
+  if (dt != QWATTN_F32 && dt != QWATTN_BF16) return fail(QWATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (p->n_q_heads <= 0 || p->n_kv_heads <= 0)
+    return fail(QWATTN_ERR_INVALID_ARG, "head counts must be positive (n_q_heads=%d, n_kv_heads=%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->n_q_heads % p->n_kv_heads != 0)
+    return fail(QWATTN_ERR_INVALID_ARG, "n_q_heads=%d is not a multiple of n_kv_heads=%d", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->head_dim != QWATTN_HEAD_DIM)
+    return fail(QWATTN_ERR_UNSUPPORTED, "head_dim=%d (only 128 is supported)", p->head_dim);
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return fail(QWATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!(p->rope_theta > 1.0) || !std::isfinite(p->rope_theta))
+    return fail(QWATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale))
+    return fail(QWATTN_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (p->order == 1) return fail(QWATTN_ERR_UNSUPPORTED, "order=1 (RoPE then norm) is not implemented");
+  if (p->order != 0) return fail(QWATTN_ERR_INVALID_ARG, "order must be 0");
+  return QWATTN_OK;
+}
+
+qwattn_status check_ptr(const void* p, const char* name, uintptr_t align = 16) {
+  if (!p) return fail(QWATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(QWATTN_ERR_INVALID_ARG, "%s is not %d-byte aligned", name, (int)align);
+  return QWATTN_OK;
+}
+
+qwattn_status check_cache(const qwattn_cache_desc* c, const void* kc, const void* vc, qwattn_dtype dt) {
+  qwattn_status st;
+  if ((st = check_ptr(kc, "k_cache")) || (st = check_ptr(vc, "v_cache"))) return st;
+  if (!c) return fail(QWATTN_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (c->capacity <= 0) return fail(QWATTN_ERR_INVALID_ARG, "cache capacity must be positive");
+  if (c->stride_seq <= 0 || c->stride_head <= 0 || c->stride_tok <= 0)
+    return fail(QWATTN_ERR_INVALID_ARG, "cache strides must be positive");
+  const int64_t es = elem_bytes(dt);
+  if ((c->stride_seq * es) % 16 || (c->stride_head * es) % 16 || (c->stride_tok * es) % 16)
+    return fail(QWATTN_ERR_INVALID_ARG, "cache strides must keep rows 16-byte aligned");
+  if (c->stride_tok < QWATTN_HEAD_DIM) return fail(QWATTN_ERR_INVALID_ARG, "cache stride_tok < head_dim");
+  return QWATTN_OK;
+}
+
+qw::RopeFreq rope_freq(double theta) {
+  qw::RopeFreq r;
+  for (int i = 0; i < qw::kHalf; ++i) r.w[i] = std::pow(theta, -(2.0 * i) / QWATTN_HEAD_DIM);
+  return r;
+}
+
+float scale_log2e(const qwattn_params* p) {
+  const double sc = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)QWATTN_HEAD_DIM);
+  return (float)(sc * 1.4426950408889634);
+}
+
+// ------------------------------------------------------------------ prefill plan
+struct PrefillPlan {
+  int g = 1, bm_tok = 1, max_tiles = 0, n_items = 0;
+  size_t off_khat = 0, off_qhat = 0, off_scratch = 0, off_items = 0, total = 0;
+};
+
+// Workspace layout; n_items / max_tiles are upper bounds when `exact` is false.
+PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, int64_t n_tok, int max_tiles,
+                           int64_t n_items, bool with_cache) {
+  PrefillPlan pl;
+  pl.g = p->n_q_heads / p->n_kv_heads;
+  const int rows = dt == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
+  pl.bm_tok = std::max(1, rows / pl.g);
+  pl.max_tiles = max_tiles;
+  pl.n_items = (int)n_items;
+  size_t off = 0;
+  pl.off_khat = off;
+  if (!with_cache) off = align256(off + (size_t)n_tok * p->n_kv_heads * QWATTN_HEAD_DIM * elem_bytes(dt));
+  pl.off_qhat = off;
+  if (dt == QWATTN_F32) off = align256(off + (size_t)n_tok * p->n_q_heads * QWATTN_HEAD_DIM * 4);
+  pl.off_scratch = off;
+  off = align256(off + (size_t)(4 * ((int64_t)max_tiles + 1) + n_seq) * 4);
+  pl.off_items = off;
+  off = align256(off + (size_t)n_items * 8);
+  pl.total = off;
+  return pl;
+}
+
+// ------------------------------------------------------------------ decode plan
+int decode_chunk(int64_t total_keys, int n_kv_heads) {
+  for (int c : {1024, 512, 256})
+    if ((total_keys / c) * n_kv_heads >= 4096) return c;
+  return qw::kDecodeKeysPerPass;
+}
+
+struct DecodeLayout {
+  int chunk = 0;
+  int64_t max_chunks = 0;
+  size_t off_qhat = 0, off_chunk = 0, off_part = 0, total = 0;
+};
+
+DecodeLayout decode_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, int64_t total_start_pos) {
+  DecodeLayout d;
+  const int64_t total_keys = total_start_pos + n_seq;
+  d.chunk = decode_chunk(total_keys, p->n_kv_heads);
+  d.max_chunks = total_keys / d.chunk + n_seq;  // >= sum_i ceil(keys_i / chunk)
+  size_t off = 0;
+  d.off_qhat = off;
+  off = align256(off + (size_t)n_seq * p->n_q_heads * QWATTN_HEAD_DIM * elem_bytes(dt));
+  d.off_chunk = off;
+  off = align256(off + (size_t)(n_seq + 1) * 4);
+  d.off_part = off;
+  if (dt == QWATTN_BF16) off = align256(off + (size_t)d.max_chunks * p->n_q_heads * qw::kPartStride * 4);
+  d.total = off;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwattn_abi_version(void) { return QWATTN_ABI_VERSION; }
+
+qwattn_status qwattn_set_timing_events(void* begin, void* end) {
+  if (!begin != !end) return fail(QWATTN_ERR_INVALID_ARG, "timing events must be both set or both NULL");
+  g_ev_begin = (hipEvent_t)begin;
+  g_ev_end = (hipEvent_t)end;
+  return QWATTN_OK;
+}
+
+const char* qwattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* qwattn_status_str(qwattn_status s) {
+  switch (s) {
+    case QWATTN_OK: return "ok";
+    case QWATTN_ERR_INVALID_ARG: return "invalid argument";
+    case QWATTN_ERR_UNSUPPORTED: return "unsupported";
+    case QWATTN_ERR_CAPACITY: return "cache capacity exceeded";
+    case QWATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case QWATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                                  const void* q_gamma, const void* k_gamma, const int32_t* positions,
+                                  int64_t n_tok, void* q_out, void* k_out, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if ((st = check_params(params, dtype))) return st;
+  if (n_tok < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_tok < 0");
+  if (!q && !k) return fail(QWATTN_ERR_INVALID_ARG, "q and k are both NULL");
+  if (!q != !q_out) return fail(QWATTN_ERR_INVALID_ARG, "q and q_out must be both set or both NULL");
+  if (!k != !k_out) return fail(QWATTN_ERR_INVALID_ARG, "k and k_out must be both set or both NULL");
+  if (q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_out, "q_out")) || (st = check_ptr(q_gamma, "q_gamma"))))
+    return st;
+  if (k && ((st = check_ptr(k, "k")) || (st = check_ptr(k_out, "k_out")) || (st = check_ptr(k_gamma, "k_gamma"))))
+    return st;
+  if ((st = check_ptr(positions, "positions", 4))) return st;
+  if (n_tok == 0) return QWATTN_OK;
+
+  qw::NormRopeArgs a{};
+  a.x[0] = q; a.x[1] = k; a.x[2] = nullptr;
+  a.out[0] = q_out; a.out[1] = k_out;
+  a.gamma[0] = q_gamma; a.gamma[1] = k_gamma;
+  a.heads[0] = q ? params->n_q_heads : 0;
+  a.heads[1] = k ? params->n_kv_heads : 0;
+  a.heads[2] = 0;
+  a.pos = positions;
+  a.mode = qw::kPosExplicit;
+  a.n_tok = n_tok;
+  a.eps = params->eps;
+  a.rope = rope_freq(params->rope_theta);
+  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
+  return QWATTN_OK;
+}
+
+size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t n_seq, int64_t n_tok,
+                                     int32_t max_seqlen, int32_t with_cache) {
+  if (check_params(params, dtype) || n_seq < 0 || n_tok < 0 || max_seqlen < 0) return 0;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  const int rows = dtype == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
+  const int bm = std::max(1, rows / g);
+  const int max_tiles = (max_seqlen + bm - 1) / bm;
+  const int64_t n_items = n_tok / bm + n_seq;
+  return prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, with_cache != 0).total;
+}
+
+qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                             const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t n_seq, void* out, void* k_cache,
+                             void* v_cache, const qwattn_cache_desc* cache, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if ((st = check_params(params, dtype))) return st;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  if (dtype == QWATTN_BF16 && g > qw::kPrefillRows)
+    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d", g, qw::kPrefillRows);
+  if (dtype == QWATTN_F32 && g > qw::kAttnF32Rows)
+    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d for fp32", g, qw::kAttnF32Rows);
+  if (n_seq < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_seq < 0");
+  if (n_seq == 0) return QWATTN_OK;
+  if (!cu_seqlens_host) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu_seqlens_host[0]);
+  int max_len = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+    if (L < 0) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d", s + 1);
+    max_len = std::max(max_len, L);
+  }
+  const int64_t n_tok = cu_seqlens_host[n_seq];
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens", 4))) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")))
+    return st;
+  const bool any_cache = k_cache || v_cache || cache;
+  if (any_cache) {
+    if ((st = check_cache(cache, k_cache, v_cache, dtype))) return st;
+    if (max_len > cache->capacity)
+      return fail(QWATTN_ERR_CAPACITY, "a sequence of %d tokens exceeds cache capacity %d", max_len, cache->capacity);
+  }
+  if (n_tok == 0) return QWATTN_OK;
+
+  const int rows = dtype == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
+  const int bm = std::max(1, rows / g);
+  int max_tiles = 0;
+  int64_t n_items = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int nt = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + bm - 1) / bm;
+    max_tiles = std::max(max_tiles, nt);
+    n_items += nt;
+  }
+  if (n_items * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many tiles");
+  const PrefillPlan pl = prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, any_cache);
+  if (pl.total > 0 && (!workspace || !aligned(workspace, 256)))
+    return fail(QWATTN_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < pl.total)
+    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, pl.total);
+
+  // ---- launches
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t D = QWATTN_HEAD_DIM;
+  const qw::RopeFreq rope = rope_freq(params->rope_theta);
+
+  // 1) norm + RoPE of K (and of Q for the fp32 path); K̂ -> cache or workspace, V -> cache
+  qw::NormRopeArgs nr{};
+  nr.x[0] = q; nr.x[1] = k; nr.x[2] = v;
+  nr.out[0] = ws + pl.off_qhat;
+  nr.out[1] = any_cache ? nullptr : (void*)(ws + pl.off_khat);
+  nr.gamma[0] = q_gamma; nr.gamma[1] = k_gamma;
+  nr.heads[0] = dtype == QWATTN_F32 ? params->n_q_heads : 0;
+  nr.heads[1] = params->n_kv_heads;
+  nr.heads[2] = any_cache ? params->n_kv_heads : 0;
+  if (any_cache) {
+    nr.k_cache = k_cache; nr.v_cache = v_cache;
+    nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
+  }
+  nr.cu = cu_seqlens;
+  nr.n_seq = n_seq;
+  nr.mode = qw::kPosPacked;
+  nr.n_tok = n_tok;
+  nr.eps = params->eps;
+  nr.rope = rope;
+  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
+  if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
+
+  // 2) tile list
+  qw::PlanArgs pa{};
+  pa.cu = cu_seqlens;
+  pa.n_seq = n_seq;
+  pa.bm_tok = bm;
+  pa.max_tiles = max_tiles;
+  pa.n_items = (int)n_items;
+  pa.scratch = (int32_t*)(ws + pl.off_scratch);
+  pa.items = (int2*)(ws + pl.off_items);
+  if ((e = qw::launch_prefill_plan(pa, strm)) != hipSuccess) return hip_fail(e, "plan launch");
+
+  // 3) attention
+  qw::PrefillArgs a{};
+  a.q = q;
+  a.q_gamma = q_gamma;
+  a.qhat = ws + pl.off_qhat;
+  if (any_cache) {
+    a.khat = k_cache;
+    a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
+    a.k_packed = 0;
+  } else {
+    a.khat = ws + pl.off_khat;
+    a.ks_seq = 0; a.ks_head = D; a.ks_tok = params->n_kv_heads * D;
+    a.k_packed = 1;
+  }
+  a.v = v;
+  a.vs_seq = 0; a.vs_head = D; a.vs_tok = params->n_kv_heads * D;
+  a.v_packed = 1;
+  a.cu = cu_seqlens;
+  a.items = pa.items;
+  a.out = out;
+  a.n_seq = n_seq;
+  a.Hq = params->n_q_heads;
+  a.Hkv = params->n_kv_heads;
+  a.g = g;
+  a.bm_tok = bm;
+  a.decode = 0;
+  a.scale_log2e = scale_log2e(params);
+  a.eps = params->eps;
+  a.rope = rope;
+  e = timed_launch(strm, [&] {
+    return dtype == QWATTN_BF16 ? qw::launch_prefill_bf16(a, (int)n_items, strm)
+                                : qw::launch_attn_f32(a, (int)n_items, strm);
+  });
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return QWATTN_OK;
+}
+
+size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t n_seq,
+                                    int64_t total_start_pos) {
+  if (check_params(params, dtype) || n_seq < 0 || total_start_pos < 0) return 0;
+  return decode_layout(params, dtype, n_seq, total_start_pos).total;
+}
+
+qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                            const void* v, const void* q_gamma, const void* k_gamma, void* k_cache, void* v_cache,
+                            const qwattn_cache_desc* cache, const int32_t* start_pos, const int32_t* start_pos_host,
+                            int32_t n_seq, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if ((st = check_params(params, dtype))) return st;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  if (dtype == QWATTN_BF16 && g > 16) return fail(QWATTN_ERR_UNSUPPORTED, "decode group size %d > 16", g);
+  if (dtype == QWATTN_F32 && g > qw::kAttnF32Rows)
+    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d for fp32", g, qw::kAttnF32Rows);
+  if (n_seq < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_seq < 0");
+  if (n_seq == 0) return QWATTN_OK;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")) ||
+      (st = check_ptr(start_pos, "start_pos", 4)))
+    return st;
+  if (!start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos_host is NULL");
+  if ((st = check_cache(cache, k_cache, v_cache, dtype))) return st;
+  int64_t total = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int sp = start_pos_host[i];
+    if (sp < 0) return fail(QWATTN_ERR_INVALID_ARG, "start_pos[%d] = %d < 0", i, sp);
+    if ((int64_t)sp + 1 > cache->capacity)
+      return fail(QWATTN_ERR_CAPACITY, "sequence %d: start_pos %d + 1 exceeds cache capacity %d", i, sp,
+                  cache->capacity);
+    total += sp;
+  }
+  const DecodeLayout dl = decode_layout(params, dtype, n_seq, total);
+  int64_t total_chunks = 0;
+  for (int i = 0; i < n_seq; ++i) total_chunks += ((int64_t)start_pos_host[i] + dl.chunk) / dl.chunk;
+  if (total_chunks * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many chunks");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(QWATTN_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < dl.total)
+    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, dl.total);
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t D = QWATTN_HEAD_DIM;
+
+  // 1) prologue: q̂ -> workspace; k̂ (rotated at start_pos) and v -> cache slot start_pos
+  qw::NormRopeArgs nr{};
+  nr.x[0] = q; nr.x[1] = k; nr.x[2] = v;
+  nr.out[0] = ws + dl.off_qhat;
+  nr.out[1] = nullptr;
+  nr.gamma[0] = q_gamma; nr.gamma[1] = k_gamma;
+  nr.heads[0] = params->n_q_heads;
+  nr.heads[1] = params->n_kv_heads;
+  nr.heads[2] = params->n_kv_heads;
+  nr.k_cache = k_cache; nr.v_cache = v_cache;
+  nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
+  nr.pos = start_pos;
+  nr.n_seq = n_seq;
+  nr.mode = qw::kPosDecode;
+  nr.n_tok = n_seq;
+  nr.eps = params->eps;
+  nr.rope = rope_freq(params->rope_theta);
+  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
+  if (e != hipSuccess) return hip_fail(e, "decode prologue launch");
+
+  if (dtype == QWATTN_BF16) {
+    qw::DecodeArgs a{};
+    a.qhat = (const uint16_t*)(ws + dl.off_qhat);
+    a.k_cache = (const uint16_t*)k_cache;
+    a.v_cache = (const uint16_t*)v_cache;
+    a.cs_seq = cache->stride_seq; a.cs_head = cache->stride_head; a.cs_tok = cache->stride_tok;
+    a.start_pos = start_pos;
+    a.chunk_off = (const int32_t*)(ws + dl.off_chunk);
+    a.partial = (float*)(ws + dl.off_part);
+    a.out = (uint16_t*)out;
+    a.n_seq = n_seq;
+    a.Hq = params->n_q_heads;
+    a.Hkv = params->n_kv_heads;
+    a.g = g;
+    a.chunk = dl.chunk;
+    a.scale_log2e = scale_log2e(params);
+    if ((e = qw::launch_decode_plan(start_pos, n_seq, dl.chunk, (int32_t*)(ws + dl.off_chunk), strm)) != hipSuccess)
+      return hip_fail(e, "decode plan launch");
+    if ((e = timed_launch(strm, [&] { return qw::launch_decode_split(a, (int)total_chunks, strm); })) != hipSuccess)
+      return hip_fail(e, "decode split launch");
+    if ((e = qw::launch_decode_combine(a, strm)) != hipSuccess) return hip_fail(e, "decode combine launch");
+  } else {
+    qw::PrefillArgs a{};
+    a.qhat = ws + dl.off_qhat;
+    a.khat = k_cache;
+    a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
+    a.k_packed = 0;
+    a.v = v_cache;
+    a.vs_seq = cache->stride_seq; a.vs_head = cache->stride_head; a.vs_tok = cache->stride_tok;
+    a.v_packed = 0;
+    a.start_pos = start_pos;
+    a.out = out;
+    a.n_seq = n_seq;
+    a.Hq = params->n_q_heads;
+    a.Hkv = params->n_kv_heads;
+    a.g = g;
+    a.bm_tok = 1;
+    a.decode = 1;
+    a.scale_log2e = scale_log2e(params);
+    a.eps = params->eps;
+    if ((e = timed_launch(strm, [&] { return qw::launch_attn_f32(a, n_seq, strm); })) != hipSuccess)
+      return hip_fail(e, "decode attention launch");
+  }
+  return QWATTN_OK;
+}
+
+}  // extern "C"

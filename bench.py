@@ -1,0 +1,251 @@
+"""Benchmark of the attention-sublayer core on one MI355X.
+
+One step = the whole hot path on synthetic Qwen3-shaped inputs resident in HBM:
+  * qwattn_prefill on the Qwen3-8B-shaped prefill (B=4 x T=4096, Hq=32, Hkv=8,
+    bf16): norm+RoPE of K into a KV cache, the tile plan, and the causal GQA
+    attention kernel with the fused Q norm+RoPE prologue;
+  * qwattn_decode on the Qwen3-8B-shaped decode (64 sequences, contexts
+    U[1024, 32768], bf16 cache): the new-token prologue, split-K attention and
+    the combine.
+Prints one JSON line.  ``value`` is prefill attention TFLOP/s (algorithmic flops:
+unmasked causal pairs only); the decode KV-read GB/s sits under ``decode``.
+
+    python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--no-decode]
+                    [--no-cpu-baseline] [--gpus 1]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (recorded by the library on its stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def setup_prefill(case_id, dev):
+    import torch
+    from attention_qk_norm_amd import binding as B, inputs
+    spec = inputs.case_spec(case_id)
+    log(f"prefill workload: {spec.workload}; generating inputs")
+    x = inputs.prefill_inputs(spec)
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(a).to(dev).to(bf)
+    st = dict(spec=spec, x=x, q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), qg=up(x["q_gamma"]), kg=up(x["k_gamma"]),
+              cu=torch.from_numpy(x["cu_seqlens"]).to(dev), cu_h=x["cu_seqlens"])
+    cap = (max(spec.lengths) + 63) // 64 * 64
+    st["kc"] = torch.empty(spec.n_seq, spec.n_kv_heads, cap, 128, dtype=bf, device=dev)
+    st["vc"] = torch.empty_like(st["kc"])
+    st["out"] = torch.empty_like(st["q"])
+    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    nbytes = B.prefill_workspace_size(p, B.BF16, spec.n_seq, spec.n_tok, max(spec.lengths), True)
+    st["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    st["params"] = p
+    return st
+
+
+def run_prefill(st):
+    from attention_qk_norm_amd import binding as B
+    B.prefill(st["params"], st["q"], st["k"], st["v"], st["qg"], st["kg"], st["cu"], st["cu_h"], out=st["out"],
+              k_cache=st["kc"], v_cache=st["vc"], workspace=st["ws"])
+
+
+def setup_decode(case_id, dev):
+    import torch
+    from attention_qk_norm_amd import binding as B, inputs
+    spec = inputs.case_spec(case_id)
+    log(f"decode workload: {spec.workload}; generating cache ({sum(spec.lengths)} tokens)")
+    x = inputs.decode_new_token(spec)
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    cap = (max(spec.lengths) + 1 + 63) // 64 * 64
+    kc = torch.zeros(spec.n_seq, spec.n_kv_heads, cap, 128, dtype=bf, device=dev)
+    vc = torch.zeros_like(kc)
+    kg = up(x["k_gamma"])
+    t0 = time.time()
+    batch = 8
+    for b0 in range(0, spec.n_seq, batch):
+        seqs = list(range(b0, min(spec.n_seq, b0 + batch)))
+        for i, (kr, vr) in zip(seqs, inputs.decode_cache_raw_all(spec, seqs)):
+            L = spec.lengths[i]
+            pos = torch.arange(L, dtype=torch.int32, device=dev)
+            _, kh = B.qk_norm_rope(p, None, up(kr), None, kg, pos)
+            kc[i, :, :L] = kh.permute(1, 0, 2)
+            vc[i, :, :L] = up(vr).permute(1, 0, 2)
+        torch.cuda.synchronize()
+    log(f"decode cache built in {time.time() - t0:.1f}s")
+    sp = x["start_pos"]
+    st = dict(spec=spec, x=x, params=p, q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), qg=up(x["q_gamma"]), kg=kg,
+              kc=kc, vc=vc, sp=torch.from_numpy(sp).to(dev), sp_h=sp)
+    st["out"] = torch.empty_like(st["q"])
+    nbytes = B.decode_workspace_size(p, B.BF16, spec.n_seq, int(sp.sum()))
+    st["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return st
+
+
+def run_decode(st):
+    from attention_qk_norm_amd import binding as B
+    B.decode(st["params"], st["q"], st["k"], st["v"], st["qg"], st["kg"], st["kc"], st["vc"], st["sp"], st["sp_h"],
+             out=st["out"], workspace=st["ws"])
+
+
+def cpu_baseline_prefill(spec):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    all query heads of 192 seeded rows of sequence 0 (keys regenerated)."""
+    import oracle
+    from attention_qk_norm_amd import accounting, inputs
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    rng = np.random.default_rng(11)
+    L = spec.lengths[0]
+    rows = np.sort(rng.choice(L, size=min(192, L), replace=False))
+    q = np.concatenate([inputs.prefill_seq_rows(spec, 0, r, r + 1, "q") for r in rows])
+    k = inputs.prefill_seq_rows(spec, 0, 0, int(rows.max()) + 1, "k")
+    v = inputs.prefill_seq_rows(spec, 0, 0, int(rows.max()) + 1, "v")
+    gq, gk = inputs.gammas(spec)
+    t0 = time.perf_counter()
+    oracle.attention_prefill_rows(q, k, v, gq, gk, rows, range(spec.n_q_heads), spec.n_q_heads,
+                                  spec.n_kv_heads, eps=spec.eps, theta=spec.theta)
+    dt = time.perf_counter() - t0
+    flops = 4 * 128 * spec.n_q_heads * int((rows + 1).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(), "blas_threads": blas_threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"all {spec.n_q_heads} query heads of {len(rows)} seeded rows of sequence 0 "
+                      f"(numpy float64 oracle; algorithmic causal flops of those rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-case", type=int, default=1, choices=[1, 3, 4])
+    ap.add_argument("--decode-case", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention core shards by KV head or sequence with no "
+              "exchange, and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_qk_norm_amd import accounting, binding as B
+    B.load()
+    dev = torch.device("cuda:0")
+    pre = setup_prefill(args.prefill_case, dev)
+    dec = None if args.no_decode else setup_decode(args.decode_case, dev)
+    ev = HipEvents()
+    n = args.steps
+    pre_ev = [(ev.create(), ev.create()) for _ in range(n)]
+    dec_ev = [(ev.create(), ev.create()) for _ in range(n)]
+    call_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+
+    def step(i=None):
+        if i is not None:
+            B.set_timing_events(*pre_ev[i])
+            call_ev[i][0].record()
+        run_prefill(pre)
+        if i is not None:
+            call_ev[i][1].record()
+        if dec is not None:
+            if i is not None:
+                B.set_timing_events(*dec_ev[i])
+                call_ev[i][2].record()
+            run_decode(dec)
+            if i is not None:
+                call_ev[i][3].record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {n} steps")
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    spec = pre["spec"]
+    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    attn_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pre_ev]))
+    pre_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in call_ev]))
+    value = flops / (pre_call_ms * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "prefill attention TFLOP/s (causal GQA with fused QK-Norm+RoPE)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(wall / n * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.workload, "global_batch": spec.n_seq, "seq_len": max(spec.lengths),
+                   "n_q_heads": spec.n_q_heads, "n_kv_heads": spec.n_kv_heads, "head_dim": 128,
+                   "rope_theta": spec.theta, "parallelism": "single-gpu",
+                   "decode_workload": None if dec is None else dec["spec"].workload},
+        "prefill_call_ms": round(pre_call_ms, 4),
+        "prefill_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(attn_ms, 4), "algorithmic_flops": flops},
+    }
+    if dec is not None:
+        ds = dec["spec"]
+        kv_bytes = accounting.decode_kv_read_bytes(ds.lengths, ds.n_kv_heads)
+        split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in dec_ev]))
+        dec_call_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in call_ev]))
+        rec["decode"] = {
+            "metric": "decode KV-read GB/s", "unit": "GB/s", "workload": ds.workload,
+            "value": round(kv_bytes / (dec_call_ms * 1e-3) / 1e9, 1), "call_ms": round(dec_call_ms, 4),
+            "frac_hbm_peak": round(kv_bytes / (dec_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_read_bytes": kv_bytes,
+            "roofline": {"kernel": "k_decode_split", "bound": "hbm",
+                         "achieved": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel_ms": round(split_ms, 4)},
+        }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline_prefill(spec)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

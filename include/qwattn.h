@@ -1,0 +1,164 @@
+/*
+ * libqwattn -- the Qwen3 attention-sublayer core on AMD MI355X (gfx950).
+ *
+ *   QK-Norm   per-head RMSNorm of Q and K: each head vector of head_dim values is
+ *             divided by sqrt(mean of its squares + eps) and multiplied by a learned
+ *             gamma of length head_dim (one for Q, one for K, shared by all heads);
+ *             the variance is taken in fp32.
+ *             ["7.2 Qwen3 全规模实现" §7.2.1 RMSNorm and GQA+QKNorm;
+ *              "Qwen3" notes, section "QK-Norm"; "第 20 章 Qwen3 与 Qwen3.5" §20.1]
+ *   RoPE      rotate-half: dims i and i + head_dim/2 of a head vector at position p
+ *             turn by the angle p * theta^(-2i/head_dim).
+ *             ["7.2 Qwen3 全规模实现" §7.2.1 RoPE]
+ *   order     QK-Norm first, then RoPE (the order four of the five pages print;
+ *             "Transformer 20. Qwen 3 架构拆解" §2.2 claims the reverse).
+ *   attention causal softmax(Q K^T / sqrt(head_dim)) V per query head t, reading
+ *             KV head floor(t / g), g = n_q_heads / n_kv_heads.
+ *             ["Transformer 20. Qwen 3 架构拆解" §2.2; "7.2 Qwen3 全规模实现" §7.2.1 GQA]
+ *   cache     holds K after norm and RoPE, and V; a new key is rotated at its own
+ *             position start_pos and never again.
+ *             ["Qwen3" notes, Qwen3Attention excerpt; "第 20 章 Qwen3 与 Qwen3.5" §20.3]
+ *
+ * Conventions for every entry point
+ *   - Device pointers are device memory of the current HIP device; host pointers
+ *     are read during the call only.  The library allocates and frees nothing:
+ *     scratch memory comes from the caller's `workspace`, sized by the
+ *     *_workspace_size functions.  All device buffers stay the caller's.
+ *   - Tensors are token-major and contiguous, head_dim innermost:
+ *     q [n_tok][n_q_heads][128], k and v [n_tok][n_kv_heads][128].  Every tensor
+ *     of a call has the call's dtype, gamma included; math is fp32; outputs
+ *     have the input dtype.  Base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it in order and the call returns without synchronising.
+ *   - Every argument is validated before anything is enqueued: on any error the
+ *     call returns a non-zero status, launches nothing and writes nothing (the
+ *     cache included), as an over-long append must leave the cache and the
+ *     position unchanged ["第 20 章 Qwen3 与 Qwen3.5" §20.9].  A failed launch
+ *     returns QWATTN_ERR_HIP; qwattn_last_error() gives the text (per thread).
+ *   - Calls are reentrant; concurrent calls must not share a workspace.
+ */
+#ifndef QWATTN_H
+#define QWATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QWATTN_ABI_VERSION 1
+#define QWATTN_HEAD_DIM 128
+
+typedef enum {
+  QWATTN_OK = 0,
+  QWATTN_ERR_INVALID_ARG = 1,  /* bad shape, pointer, alignment or length array   */
+  QWATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim != 128, ...) */
+  QWATTN_ERR_CAPACITY = 3,     /* a sequence would not fit in the cache           */
+  QWATTN_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required      */
+  QWATTN_ERR_HIP = 5           /* a HIP runtime call or launch failed             */
+} qwattn_status;
+
+typedef enum { QWATTN_F32 = 0, QWATTN_BF16 = 1 } qwattn_dtype;
+
+typedef struct {
+  int32_t n_q_heads;    /* query heads, > 0                                        */
+  int32_t n_kv_heads;   /* KV heads, > 0, divides n_q_heads; g = n_q / n_kv <= 128  */
+  int32_t head_dim;     /* must be 128                                             */
+  float eps;            /* RMSNorm epsilon (1e-6 for Qwen3), >= 0                  */
+  double rope_theta;    /* RoPE base (1e6 dense Qwen3, 1e7 for the MoE models), > 1 */
+  float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                   */
+  int32_t order;        /* 0 = QK-Norm then RoPE (the only value accepted)         */
+} qwattn_params;
+
+/* A KV cache: element (seq s, kv head h, slot j, dim d) of k_cache / v_cache is at
+ * base + s*stride_seq + h*stride_head + j*stride_tok + d (strides in elements;
+ * dim innermost and contiguous; stride_tok * elem_size and every other stride
+ * must keep rows 16-byte aligned).  Slots 0 .. capacity-1 exist per sequence. */
+typedef struct {
+  int64_t stride_seq;
+  int64_t stride_head;
+  int64_t stride_tok;
+  int32_t capacity;
+} qwattn_cache_desc;
+
+/* QK-Norm then RoPE on standalone rows.
+ *   q [n_tok][n_q_heads][128] and k [n_tok][n_kv_heads][128] (device): raw rows;
+ *     either may be NULL (then its output must be NULL too).
+ *   q_gamma, k_gamma [128] (device): the learned scales; required with q / k.
+ *   positions [n_tok] (device int32, >= 0): position of each token row.
+ *   q_out, k_out (device): same shapes; may alias q, k (in place).
+ * n_tok == 0 is a no-op.  Used on its own and to fill a cache with rotated keys. */
+qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtype,
+                                  const void* q, const void* k,
+                                  const void* q_gamma, const void* k_gamma,
+                                  const int32_t* positions, int64_t n_tok,
+                                  void* q_out, void* k_out, void* stream);
+
+/* Causal GQA prefill over packed ragged sequences, with QK-Norm and RoPE fused.
+ *   q [n_tok][n_q_heads][128], k, v [n_tok][n_kv_heads][128] (device): raw rows of
+ *     all sequences packed one after another.
+ *   cu_seqlens [n_seq+1] (device int32) and cu_seqlens_host (host, same values):
+ *     sequence s owns tokens cu[s] .. cu[s+1]-1 at positions 0 .. L_s-1; cu[0] = 0,
+ *     non-decreasing, cu[n_seq] = n_tok.  Sequences never attend to each other.
+ *   out [n_tok][n_q_heads][128] (device): attention output (before o_proj).
+ *   k_cache, v_cache, cache (optional, all NULL or all set): K after norm and RoPE
+ *     and V of sequence s, token j go to slot j of cache sequence s; every
+ *     L_s <= capacity.
+ *   workspace (device, >= qwattn_prefill_workspace_size bytes, 256-byte aligned).
+ * n_tok == 0 or n_seq == 0 is a no-op. */
+qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype,
+                             const void* q, const void* k, const void* v,
+                             const void* q_gamma, const void* k_gamma,
+                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                             int32_t n_seq, void* out,
+                             void* k_cache, void* v_cache, const qwattn_cache_desc* cache,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* One new token per sequence against a KV cache (split-K decode).
+ *   q [n_seq][n_q_heads][128], k, v [n_seq][n_kv_heads][128] (device): the raw
+ *     new token of each sequence.
+ *   k_cache, v_cache, cache: slots 0 .. start_pos[i]-1 of sequence i hold K after
+ *     norm and RoPE and V.  The call normalises and rotates the new k at position
+ *     start_pos[i], writes it and v into slot start_pos[i] (never re-rotating the
+ *     old keys), and attends over the start_pos[i] + 1 keys.
+ *   start_pos [n_seq] (device int32) and start_pos_host (host, same values):
+ *     >= 0 and start_pos[i] + 1 <= capacity for every i, else QWATTN_ERR_CAPACITY
+ *     with nothing written.
+ *   out [n_seq][n_q_heads][128] (device).
+ *   workspace (device, >= qwattn_decode_workspace_size bytes, 256-byte aligned).
+ * n_seq == 0 is a no-op. */
+qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
+                            const void* q, const void* k, const void* v,
+                            const void* q_gamma, const void* k_gamma,
+                            void* k_cache, void* v_cache, const qwattn_cache_desc* cache,
+                            const int32_t* start_pos, const int32_t* start_pos_host,
+                            int32_t n_seq, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qwattn_prefill needs for these sizes (0 on invalid params).
+ * with_cache != 0 when the call will pass a cache (the rotated K goes there). */
+size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
+                                     int32_t n_seq, int64_t n_tok, int32_t max_seqlen,
+                                     int32_t with_cache);
+
+/* Workspace bytes qwattn_decode needs for n_seq sequences whose start positions
+ * sum to total_start_pos (0 on invalid params). */
+size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
+                                    int32_t n_seq, int64_t total_start_pos);
+
+/* Timing hook for benchmarks and profilers.  `begin` and `end` are hipEvent_t
+ * handles (or both NULL to clear).  The calling thread's next qwattn_prefill or
+ * qwattn_decode records `begin` on its stream right before its dominant kernel
+ * (the attention kernel of prefill, the split kernel of decode) and `end` right
+ * after it, then clears the hook.  Setting it enqueues nothing. */
+qwattn_status qwattn_set_timing_events(void* begin, void* end);
+
+const char* qwattn_status_str(qwattn_status status); /* static string             */
+const char* qwattn_last_error(void);                 /* this thread's last detail */
+int qwattn_abi_version(void);                        /* QWATTN_ABI_VERSION        */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QWATTN_H */

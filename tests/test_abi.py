@@ -1,0 +1,123 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, and rejects invalid calls before touching a GPU (no call here
+reaches a HIP runtime function: validation fails first)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_qk_norm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"qwattn_qk_norm_rope", "qwattn_prefill", "qwattn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qwattn_abi_version() == 1
+    for st in range(6):
+        assert lib.qwattn_status_str(st)
+
+
+F = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x100002)
+
+
+def cu(*vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def prefill(lib, p, cu_h, n_seq, q=F, cache=(None, None, None), ws=F, ws_bytes=1 << 30, dtype=1):
+    kc, vc, d = cache
+    return lib.qwattn_prefill(ctypes.byref(p), dtype, q, F, F, F, F, F, cu_h, n_seq, F, kc, vc,
+                              ctypes.byref(d) if d is not None else None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=30, n_kv_heads=8), B.ERR_INVALID_ARG),
+    (dict(n_q_heads=0, n_kv_heads=8), B.ERR_INVALID_ARG),
+    (dict(n_q_heads=32, n_kv_heads=8, head_dim=64), B.ERR_UNSUPPORTED),
+    (dict(n_q_heads=32, n_kv_heads=8, order=1), B.ERR_UNSUPPORTED),
+    (dict(n_q_heads=32, n_kv_heads=8, order=2), B.ERR_INVALID_ARG),
+    (dict(n_q_heads=32, n_kv_heads=8, rope_theta=1.0), B.ERR_INVALID_ARG),
+    (dict(n_q_heads=32, n_kv_heads=8, eps=-1.0), B.ERR_INVALID_ARG),
+])
+def test_bad_params(lib, kw, status):
+    p = B.make_params(**kw)
+    assert prefill(lib, p, cu(0, 5), 1) == status
+    assert lib.qwattn_last_error()
+
+
+def test_bad_lengths_pointers_workspace(lib):
+    p = B.make_params(32, 8)
+    assert prefill(lib, p, cu(1, 5), 1) == B.ERR_INVALID_ARG          # cu[0] != 0
+    assert prefill(lib, p, cu(0, 5, 3), 2) == B.ERR_INVALID_ARG       # decreasing
+    assert prefill(lib, p, cu(0, 5), 1, q=ODD) == B.ERR_INVALID_ARG   # misaligned
+    assert prefill(lib, p, cu(0, 5), 1, q=None) == B.ERR_INVALID_ARG  # NULL
+    assert prefill(lib, p, cu(0, 5), 1, ws_bytes=16) == B.ERR_WORKSPACE
+    assert prefill(lib, p, cu(0, 5), 1, ws=None) == B.ERR_WORKSPACE
+    d = B.CacheDesc(8 * 4 * 128, 4 * 128, 128, 4)                      # capacity 4 < 5 tokens
+    assert prefill(lib, p, cu(0, 5), 1, cache=(F, F, d)) == B.ERR_CAPACITY
+    assert prefill(lib, p, cu(0, 5), 1, cache=(F, None, d)) == B.ERR_INVALID_ARG
+    d2 = B.CacheDesc(8 * 8 * 130, 8 * 130, 130, 8)                     # rows not 16-byte aligned
+    assert prefill(lib, p, cu(0, 5), 1, cache=(F, F, d2)) == B.ERR_INVALID_ARG
+    assert prefill(lib, p, cu(0), 0) == B.OK                           # n_seq = 0: no-op
+    assert prefill(lib, B.make_params(256, 1), cu(0, 5), 1) == B.ERR_UNSUPPORTED
+
+
+def test_decode_capacity_overflow_rejected(lib):
+    """An append past the cache capacity is an error with nothing enqueued."""
+    p = B.make_params(32, 8)
+    d = B.CacheDesc(8 * 100 * 128, 100 * 128, 128, 100)
+    sp = cu(3, 99, 100)
+    r = lib.qwattn_decode(ctypes.byref(p), 1, F, F, F, F, F, F, F, ctypes.byref(d), F, sp, 3, F, F, 1 << 30, None)
+    assert r == B.ERR_CAPACITY
+    assert b"sequence 2" in lib.qwattn_last_error()
+    sp = cu(3, -1)
+    r = lib.qwattn_decode(ctypes.byref(p), 1, F, F, F, F, F, F, F, ctypes.byref(d), F, sp, 2, F, F, 1 << 30, None)
+    assert r == B.ERR_INVALID_ARG
+    r = lib.qwattn_decode(ctypes.byref(B.make_params(64, 2)), 1, F, F, F, F, F, F, F, ctypes.byref(d), F,
+                          cu(3), 1, F, F, 1 << 30, None)
+    assert r == B.ERR_UNSUPPORTED  # g = 32 > 16 on the bf16 decode path
+
+
+def test_workspace_sizes(lib):
+    p = B.make_params(32, 8)
+    a = B.prefill_workspace_size(p, B.BF16, 4, 16384, 4096, False)
+    b = B.prefill_workspace_size(p, B.BF16, 4, 16384, 4096, True)
+    assert a > b > 0
+    assert a - b >= 16384 * 8 * 128 * 2  # the rotated-K buffer when no cache is given
+    assert B.prefill_workspace_size(B.make_params(30, 8), B.BF16, 4, 16384, 4096, False) == 0
+    assert B.decode_workspace_size(p, B.BF16, 64, 1 << 20) > 64 * 32 * 128 * 2
+    assert B.decode_workspace_size(p, 7, 64, 1 << 20) == 0
+
+
+def test_qk_norm_rope_validation(lib):
+    p = B.make_params(8, 2)
+    f = lib.qwattn_qk_norm_rope
+    assert f(ctypes.byref(p), 1, None, None, F, F, F, 10, None, None, None) == B.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), 1, F, None, F, F, F, 10, None, None, None) == B.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), 1, F, None, F, None, F, -1, F, None, None) == B.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), 1, F, None, F, None, F, 0, F, None, None) == B.OK
