@@ -7,49 +7,67 @@
 // (done here, in the prologue) and k read already normed and rotated (written by
 // the norm+RoPE pass into the cache or the workspace).
 //
-// Layout of the work: a workgroup (4 waves) owns one KV head u of one sequence
-// and a query tile of bm_tok tokens x g heads = up to 128 rows, so every K/V
-// tile staged in LDS serves all g heads of the group.  Each wave holds 32 rows.
+// Work layout: a workgroup (4 waves) owns one KV head u of one sequence and a
+// query tile of bm_tok tokens x g heads = up to 256 rows, so every K/V tile
+// staged in LDS serves all g heads of the group.  Each wave holds 64 rows as two
+// 32-row blocks, so every K or V fragment it reads from LDS feeds two MFMAs (the
+// LDS pipe, not the bytes, limits the fragment reads on gfx950).
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // A = a K fragment from LDS, B = the wave's resident bf16 Q fragments.  In the
 // 32x32 accumulator each lane then owns ONE query row (lane % 32) and 16 keys,
-// so the softmax max and sum are lane-local plus one lane-half swap, and the
-// accumulator, rounded to bf16, is directly the B operand of O^T = V^T P^T once
-// the key order inside each 16-key slice is permuted consistently on the V side.
-// V stays row-major in LDS; its transposed A operand comes from gfx950's
-// ds_read_b64_tr_b16 (two per fragment).  Online softmax in fp32 with exp2 and
-// log2(e) folded into the scale; tiles entirely above the diagonal are never
-// visited, and only tiles crossing it are masked.
+// so the softmax is lane-local plus one lane-pair exchange, and the
+// probabilities, rounded to bf16, are directly the B operand of O^T = V^T P^T
+// once the key order inside each 16-key slice is permuted the same way on the V
+// side.  V stays row-major in LDS; its transposed A operand comes from gfx950's
+// ds_read_b64_tr_b16 (two per fragment).
+//
+// K/V tiles of 64 keys go HBM -> LDS directly (global_load_lds_dwordx4, no
+// staging registers) into a two-stage ring: tile t+1 lands while tile t is used.
+//
+// Softmax: QK-Norm bounds every logit.  With q^ the bf16 query row and every
+// rotated key of norm <= sqrt(128) max|gamma_k| (RoPE keeps norms), the scaled
+// score is at most B = scale * |q^| * sqrt(128) * max|gamma_k| (plus a margin
+// for bf16 rounding).  p = 2^(s log2e - B) then needs no running max and no
+// rescaling of the accumulators, and stays a normal float as long as B <= 60
+// (in log2 units).  A wave with any larger bound runs the usual online softmax.
+// Both are exactly softmax; only rounding differs.  Tiles entirely above a
+// wave's diagonal are skipped; only tiles crossing it are masked.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qw {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kRowBytes = kD * 2;  // one bf16 row in LDS
+constexpr float kStaticBoundMax = 60.f;             // log2 units
 
+// LDS tile layout.  Row r of a 64-row tile lives in 1 KB block r % 16, slot
+// r / 16 (256 B per slot); blocks are padded apart (K: 1040 B, V: 1088 B).
+// A direct global->LDS load fills one whole block (lane l -> slot l / 16,
+// 16-byte chunk l % 16).  Every fragment read is then one per-lane base plus
+// compile-time offsets, and the rows read together land in distinct banks:
+//  * K (b128 reads, 16 consecutive rows at one chunk): the 16 B block skew
+//    spreads the 16 rows over all 16 chunk slots of a 256 B bank line;
+//  * V (transposed b64 reads, 4 consecutive rows x 64 B per half-wave): the
+//    64 B block skew puts the 4 rows in the 4 windows of a bank line.
+constexpr int kKBlk = 1040, kVBlk = 1088;
+constexpr int kKTile = 16 * kKBlk, kVTile = 16 * kVBlk;
+constexpr int kStageBytes = kKTile + kVTile;
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
 }
 
-// Byte offset of (row, 16-byte chunk) in a K tile: chunk ^ (row & 15) makes the
-// 32 rows of one MFMA fragment read hit 16 distinct chunk slots per 16 lanes.
-__device__ __forceinline__ int k_swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 15)) << 4);
-}
-// V tile: the transposed reads touch 8 consecutive rows x 64 bytes; XOR-ing the
-// chunk with (row & 3) << 2 puts the 4 rows of each half-wave in different
-// 64-byte bank windows.
-__device__ __forceinline__ int v_swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ ((row & 3) << 2)) << 4);
+__device__ __forceinline__ void load_lds16(const void* g, lds_u8* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
 
 __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kTileKeys * kRowBytes];
-  lds_u8* ks = (lds_u8*)(smem);
-  lds_u8* vs = ks + kTileKeys * kRowBytes;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (K, V)
+  lds_u8* lds = (lds_u8*)(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -63,26 +81,57 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   if (qt < 0 || tok_base >= L) return;
   const int n_kv = min(L, tok_base + a.bm_tok);
 
-  // ---- this lane's query row
+  // ---- this lane's two query rows (blocks qb = 0, 1 of the wave)
   const int n = lane & 31, hg = lane >> 5;
-  const int r = w * 32 + n;
-  const int hoff = r / a.bm_tok, toff = r - hoff * a.bm_tok;
-  const int qtok = tok_base + toff;
-  const bool valid = hoff < a.g && qtok < L;
-  const int qpos = valid ? qtok : 0x3fffffff;  // padding rows see every key
-  const int t_head = u * a.g + hoff;
-  int wave_min = qpos;
+  int qpos[2], qtok[2], t_head[2];
+  bool valid[2];
+  int wave_min = 0x3fffffff, wave_max = -1;
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1) wave_min = min(wave_min, __shfl_xor(wave_min, m, 64));
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = w * 64 + qb * 32 + n;
+    const int hoff = r / a.bm_tok, toff = r - hoff * a.bm_tok;
+    qtok[qb] = tok_base + toff;
+    valid[qb] = hoff < a.g && qtok[qb] < L;
+    qpos[qb] = valid[qb] ? qtok[qb] : 0x3fffffff;  // padding rows see every key
+    t_head[qb] = u * a.g + hoff;
+    wave_min = min(wave_min, qpos[qb]);
+    wave_max = max(wave_max, valid[qb] ? qtok[qb] : -1);
+  }
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    wave_min = min(wave_min, __shfl_xor(wave_min, m, 64));
+    wave_max = max(wave_max, __shfl_xor(wave_max, m, 64));
+  }
 
-  // ---- prologue: QK-Norm + RoPE of the query row, kept as bf16 MFMA fragments.
+  // ---- prologue: QK-Norm + RoPE of each query row, kept as bf16 MFMA fragments.
   // Lane (n, hg) holds dims 16kk + 8hg + e (kk < 8, e < 8); dims i and i + 64 of
   // a rotation pair sit in fragments kk and kk + 4 of the same lane.
-  bf16x8 qf[8];
+  bf16x8 qf[2][8];
+  float bound[2];
+  // max |gamma| of q and k: every rotated query row then has norm <=
+  // sqrt(128) max|gamma_q| and every key <= sqrt(128) max|gamma_k|, which bounds
+  // all logits of the launch by the same number in every wave.
+  float kmax, qmax;
   {
+    const uint16_t* gk = (const uint16_t*)a.k_gamma;
+    const uint16_t* gq = (const uint16_t*)a.q_gamma;
+    kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * lane])), fabsf(bf16_to_f32(gk[2 * lane + 1])));
+    qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * lane])), fabsf(bf16_to_f32(gq[2 * lane + 1])));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
+      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
+    }
+  }
+  const float bound_scale = a.scale_log2e * 11.313708498984761f * kmax * (1.0f + 1.0f / 128);
+  const bool use_static = bound_scale * 11.313708498984761f * qmax * (1.0f + 1.0f / 128) <= kStaticBoundMax;
+  // QK-Norm + RoPE of one query row into bf16 fragments; returns the row's logit
+  // bound.  Called once per query block with static arguments, so the fragment
+  // arrays stay in registers.
+  auto row_prologue = [&](bool ok, int tok, int head, bf16x8 (&frag)[8]) __attribute__((always_inline)) {
     float x[8][8];
-    if (valid) {
-      const uint16_t* src = (const uint16_t*)a.q + ((int64_t)(seq0 + qtok) * a.Hq + t_head) * kD + 8 * hg;
+    if (ok) {
+      const uint16_t* src = (const uint16_t*)a.q + ((int64_t)(seq0 + tok) * a.Hq + head) * kD + 8 * hg;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * kk);
@@ -115,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk][2 * e + 1] *= inv * bf16_hi(gr[e]);
       }
     }
-    const int p = valid ? qtok : 0;
+    const int p = ok ? tok : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -127,11 +176,23 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk + 4][e] = y2 * c + y1 * sn;
       }
     }
+    float qn = 0.f;  // squared norm of the bf16 row that the MFMAs will see
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 w4;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)x[kk][e];
-  }
+      for (int e = 0; e < 4; ++e) {
+        w4[e] = pack_bf16x2(x[kk][2 * e], x[kk][2 * e + 1]);
+        const float f0 = bf16_lo(w4[e]), f1 = bf16_hi(w4[e]);
+        qn += f0 * f0 + f1 * f1;
+      }
+      frag[kk] = __builtin_bit_cast(bf16x8, w4);
+    }
+    return sqrtf(pair_sum(qn)) * bound_scale;
+  };
+  bound[0] = row_prologue(valid[0], qtok[0], t_head[0], qf[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  bound[1] = row_prologue(valid[1], qtok[1], t_head[1], qf[1]);
 
   // ---- K/V sources for (sequence s, KV head u)
   const uint16_t* kbase = (const uint16_t*)a.khat + u * a.ks_head +
@@ -139,138 +200,165 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const uint16_t* vbase = (const uint16_t*)a.v + u * a.vs_head +
                           (a.v_packed ? (int64_t)seq0 * a.vs_tok : (int64_t)s * a.vs_seq);
 
-  // Each thread stages 4 of the 1024 16-byte chunks of a 64-key K tile and of V.
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
+  // Each wave fills blocks 4w .. 4w+3 of K and of V per tile.  Keys past n_kv
+  // repeat the last key: they are masked, and stay finite.
+  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    lds_u8* kdst = lds + stage * kStageBytes;
+    lds_u8* vdst = kdst + kKTile;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int c = tid + 256 * m;
-      const int row = c >> 4, col = c & 15;
-      const int key = t * kTileKeys + row;
-      if (key < n_kv) {
-        kreg[m] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * a.ks_tok + col * 8);
-        vreg[m] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * a.vs_tok + col * 8);
-      } else {
-        kreg[m] = u32x4{0, 0, 0, 0};
-        vreg[m] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int c = tid + 256 * m;
-      const int row = c >> 4, col = c & 15;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(ks + k_swz(row, col)) = kreg[m];
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vs + v_swz(row, col)) = vreg[m];
+      const int blk = w * 4 + m;
+      const int row = blk + 16 * (lane >> 4);
+      const int col = (lane & 15) * 8;
+      const int key = min(t * kTileKeys + row, n_kv - 1);
+      load_lds16(kbase + (int64_t)key * a.ks_tok + col, kdst + blk * kKBlk);
+      load_lds16(vbase + (int64_t)key * a.vs_tok + col, vdst + blk * kVBlk);
     }
   };
 
-  f32x16 o[4];
+  f32x16 o[2][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[qb][db][j] = 0.f;
+  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
 
-  // transposed-read coordinates of this lane inside a V tile (see the header)
+  // Per-lane LDS bases of the fragment reads (everything else is an immediate).
+  // K: row 32kb + n, chunk 2kk + hg.  V (transposed): row 16kk + v_row0 (+8),
+  // dims 32db + v_col0 .. +3.
   const int G = lane >> 4, lam = lane & 15;
-  const int v_row0 = 4 * (G >> 1) + (lam >> 2);    // + 16 kk (+ 8 for the upper half)
-  const int v_col0 = 16 * (G & 1) + 4 * (lam & 3);  // + 32 db, in elements
+  const int v_row0 = 4 * (G >> 1) + (lam >> 2);
+  const int v_col0 = 16 * (G & 1) + 4 * (lam & 3);
+  const int k_base = (n & 15) * kKBlk + (n >> 4) * 256 + hg * 16;
+  const int v_base = v_row0 * kVBlk + v_col0 * 2;
 
   const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  const float c_log2 = a.scale_log2e;
 
-    // S^T = K Q^T for the tile's two 32-key blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-      const int krow = 32 * kb + n;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = lds_load_b128(ks + k_swz(krow, 2 * kk + hg));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // online softmax; sacc[kb][j] is key 64t + 32kb + 8(j/4) + 4hg + j%4 of row n
-    const int key0 = t * kTileKeys;
-    const bool diag = key0 + kTileKeys - 1 > wave_min;
-    float sv[32];
-    float mt = -INFINITY;
+  // One tile: S^T = K Q^T, softmax in place on the accumulators, O^T += V^T P^T.
+  auto tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto static_tag) __attribute__((always_inline)) {
+    constexpr bool kStatic = decltype(static_tag)::value;
+    f32x16 sacc[2][2];  // [key block kb][query block qb]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = sacc[kb][j] * a.scale_log2e;
-        if (diag) {
-          const int key = key0 + 32 * kb + 8 * (j >> 2) + 4 * hg + (j & 3);
-          if (key > qpos) x = -INFINITY;
-        }
-        sv[kb * 16 + j] = x;
-        mt = fmaxf(mt, x);
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[kb][qb][j] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], sacc[kb][qb], 0, 0, 0);
       }
-    mt = pair_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(sv[i] - m_new);
-      sv[i] = pv;
-      psum += pv;
     }
-    l_run = l_run * alpha + psum;
+    // sacc[kb][qb][j] is key key0 + 32kb + 8(j/4) + 4hg + j%4 of row (qb, n)
+    const bool diag = key0 + kTileKeys - 1 > wave_min;
+    bf16x8 pf[2][4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+      if (diag) {  // key0 + 32kb + 8(j/4) + 4hg + j%4 > qpos  <=>  constant > lim
+        const int lim = qpos[qb] - key0 - 4 * hg;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-
-    // P^T fragments: slice kk (16 keys) = registers 8(kk%2) .. +7 of block kk/2
-    bf16x8 pf[4];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+          for (int j = 0; j < 16; ++j)
+            if (32 * kb + 8 * (j >> 2) + (j & 3) > lim) sacc[kb][qb][j] = -INFINITY;
+      }
+      float m_use;
+      if constexpr (kStatic) {
+        m_use = bound[qb];
+      } else {
+        float mt = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[kk][i] = (__bf16)sv[(kk >> 1) * 16 + 8 * (kk & 1) + i];
-
-    // O^T += V^T P^T; the A operand (V^T rows d, keys in the permuted slice order)
-    // comes from two transposed 8-byte LDS reads per fragment.
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+          for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[kb][qb][j]);
+        mt = pair_max(mt) * c_log2;
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[qb][db][j] *= alpha;
+        m_use = m_new;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          sacc[kb][qb][j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][j], c_log2, -m_use));
+      // P^T fragments: slice kk (16 keys) = registers 8(kk%2) .. +7 of block kk/2.
+      // The row sum adds the bf16-rounded weights the MFMA uses, so every output
+      // row is an exact convex combination of V rows.
+      float psum = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int row = 16 * kk + v_row0;
-        const int col = 32 * db + v_col0;
-        const int off = (col & 7) * 2;
-        const bf16x8 va = concat_tr16(lds_read_tr16(vs + v_swz(row, col >> 3) + off),
-                                      lds_read_tr16(vs + v_swz(row + 8, col >> 3) + off));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kk], o[db], 0, 0, 0);
+        u32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w4[e] = pack_bf16x2(sacc[kk >> 1][qb][8 * (kk & 1) + 2 * e], sacc[kk >> 1][qb][8 * (kk & 1) + 2 * e + 1]);
+          psum += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+        }
+        pf[qb][kk] = __builtin_bit_cast(bf16x8, w4);
+      }
+      l_run[qb] += psum;
+    }
+    // O^T += V^T P^T; each V fragment (two transposed reads) feeds both query blocks
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const lds_u8* vp = vs + v_base + kk * 256 + db * 64;
+        const bf16x8 va = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][kk], o[qb][db], 0, 0, 0);
       }
     }
-  }
+  };
 
-  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of row n
-  const float l_tot = pair_sum(l_run);
-  const float inv_l = 1.0f / l_tot;
-  if (valid) {
-    uint16_t* dst = (uint16_t*)a.out + ((int64_t)(seq0 + qtok) * a.Hq + t_head) * kD;
+  auto run = [&](auto static_tag) __attribute__((always_inline)) {
+    issue_tile(0, 0);
+    for (int t = 0; t < n_tiles; ++t) {
+      const int stage = t & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile t is in LDS
+      __syncthreads();                      // ... everyone's, and tile t-1's stage is free
+      if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
+      const int key0 = t * kTileKeys;
+      if (key0 > wave_max) continue;        // every key of the tile is in this wave's future
+      const lds_u8* ks = lds + stage * kStageBytes;
+      tile(ks, ks + kKTile, key0, static_tag);
+    }
+  };
+  if (use_static)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of row (qb, n)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float inv_l = 1.0f / pair_sum(l_run[qb]);
+    if (valid[qb]) {
+      uint16_t* dst = (uint16_t*)a.out + ((int64_t)(seq0 + qtok[qb]) * a.Hq + t_head[qb]) * kD;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d = 32 * db + 8 * jg + 4 * hg;
-        u32x2 pk = {pack_bf16x2(o[db][4 * jg] * inv_l, o[db][4 * jg + 1] * inv_l),
-                    pack_bf16x2(o[db][4 * jg + 2] * inv_l, o[db][4 * jg + 3] * inv_l)};
-        *reinterpret_cast<u32x2*>(dst + d) = pk;
-      }
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int d = 32 * db + 8 * jg + 4 * hg;
+          u32x2 pk = {pack_bf16x2(o[qb][db][4 * jg] * inv_l, o[qb][db][4 * jg + 1] * inv_l),
+                      pack_bf16x2(o[qb][db][4 * jg + 2] * inv_l, o[qb][db][4 * jg + 3] * inv_l)};
+          *reinterpret_cast<u32x2*>(dst + d) = pk;
+        }
+    }
   }
 }
 
@@ -344,8 +432,11 @@ hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+  if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), 2 * kStageBytes, st, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
 struct PrefillArgs {
   const void* q;            // raw [n_tok][Hq][128]
   const void* q_gamma;
+  const void* k_gamma;      // bf16 path: bounds the rotated-key norms
   const void* qhat;         // fp32 path: normed+rotated q [n_tok][Hq][128] (fp32)
   const void* khat;         // rotated keys; row (s, h, j) at khat + h*ks_head + base(s) + j*ks_tok
   int64_t ks_seq, ks_head, ks_tok;
@@ -69,7 +70,7 @@ struct PrefillArgs {
   float eps;
   RopeFreq rope;
 };
-constexpr int kPrefillRows = 128;  // query rows (g heads x bm_tok tokens) per workgroup
+constexpr int kPrefillRows = 256;  // query rows (g heads x bm_tok tokens) per workgroup
 constexpr int kAttnF32Rows = 64;   // fp32 path: query rows per workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st);
 hipError_t launch_attn_f32(const PrefillArgs& a, int n_items, hipStream_t st);

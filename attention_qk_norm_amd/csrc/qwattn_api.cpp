@@ -326,6 +326,7 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, co
   qw::PrefillArgs a{};
   a.q = q;
   a.q_gamma = q_gamma;
+  a.k_gamma = k_gamma;
   a.qhat = ws + pl.off_qhat;
   if (any_cache) {
     a.khat = k_cache;
