@@ -45,6 +45,41 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double w, float& c, float&
   sincosf((float)r, &s, &c);
 }
 
+// Sum over each group of 16 consecutive lanes (one DPP row): butterfly within
+// quads, then rotations by 4 and 8 inside the row; every lane ends with the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror 4
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror 8
+  return x;
+}
+
+// Exclusive prefix sum over a 1024-thread block (each thread one value);
+// `tmp` is 16 ints of LDS.  Returns the thread's exclusive prefix and writes the
+// block total to *total.  Every thread of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  int wsum = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tmp[i];
+    wsum += i < w ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return wsum + inc - v;
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float x) {

@@ -191,16 +191,23 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   }
 }
 
-// One wave per (sequence, query head): merge its chunks' partials.
+// One wave per (sequence, query head): merge its chunks' partials.  The lanes
+// first take the chunks' maxima in parallel; the weighted sum then walks the
+// chunks with four loads in flight, each lane owning two of the 128 dims.
 __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
   const int i = blockIdx.x / a.Hq, t = blockIdx.x % a.Hq;
   const int lane = threadIdx.x;
   const int c0 = a.chunk_off[i], c1 = a.chunk_off[i + 1];
+  const float* base = a.partial + t * kPartStride;
+  const int64_t cstride = (int64_t)a.Hq * kPartStride;
   float M = -1e30f;
-  for (int c = c0; c < c1; ++c) M = fmaxf(M, a.partial[((int64_t)c * a.Hq + t) * kPartStride + kD]);
+  for (int c = c0 + lane; c < c1; c += 64) M = fmaxf(M, base[c * cstride + kD]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+#pragma unroll 4
   for (int c = c0; c < c1; ++c) {
-    const float* p = a.partial + ((int64_t)c * a.Hq + t) * kPartStride;
+    const float* p = base + c * cstride;
     const float f = __builtin_amdgcn_exp2f(p[kD] - M);
     lsum += f * p[kD + 1];
     acc0 += f * p[2 * lane];
@@ -213,22 +220,17 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
 // chunk_off[i] = sum_{i' < i} ceil((start_pos[i'] + 1) / chunk); one workgroup.
 __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* start_pos, int n_seq, int chunk,
                                                       int32_t* chunk_off) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int per = (n_seq + 1023) / 1024;
-  const int lo = min(n_seq, tid * per), hi = min(n_seq, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += (start_pos[i] + chunk) / chunk;
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int i = 0; i < 1024; ++i) { const int v = part[i]; part[i] = acc; acc += v; }
-    chunk_off[n_seq] = acc;
+  __shared__ int tmp[16];
+  int carry = 0;
+  for (int base = 0; base < n_seq; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int v = i < n_seq ? (start_pos[i] + chunk) / chunk : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, tmp, &total);
+    if (i < n_seq) chunk_off[i] = carry + ex;
+    carry += total;
   }
-  __syncthreads();
-  int acc = part[tid];
-  for (int i = lo; i < hi; ++i) { chunk_off[i] = acc; acc += (start_pos[i] + chunk) / chunk; }
+  if (threadIdx.x == 0) chunk_off[n_seq] = carry;
 }
 
 }  // namespace

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
 // Lengths are clamped to what the host sized, so a device/host mismatch cannot
 // write out of bounds.
 __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
-  __shared__ int part[1024];
+  __shared__ int tmp[16];
   const int tid = threadIdx.x;
   const int nb = a.max_tiles + 1;
   int32_t* hist = a.scratch;
@@ -389,23 +389,21 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
   __syncthreads();
   for (int s = tid; s < a.n_seq; s += 1024) atomicAdd(&hist[n_tiles_of(s)], 1);
   __syncthreads();
-  // two suffix sums: cnt_gt[q] = sum_{n > q} hist[n]; off[q] = sum_{q' > q} cnt_gt[q']
-  const int per = (nb + 1023) / 1024;
+  // two suffix sums, 1024 entries at a time from the top (thread order runs
+  // from high to low index, so a prefix scan over threads is a suffix sum):
+  //   cnt_gt[q] = sum_{n > q} hist[n];  off[q] = sum_{q' > q} cnt_gt[q']
   for (int pass = 0; pass < 2; ++pass) {
     const int32_t* in = pass == 0 ? hist : cnt_gt;
     int32_t* outp = pass == 0 ? cnt_gt : off;
-    const int lo = min(nb, tid * per), hi = min(nb, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += in[i];
-    part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {  // exclusive suffix over the 1024 partial sums
-      int acc = 0;
-      for (int i = 1023; i >= 0; --i) { const int v = part[i]; part[i] = acc; acc += v; }
+    int carry = 0;
+    for (int base = ((nb - 1) / 1024) * 1024; base >= 0; base -= 1024) {
+      const int i = base + 1023 - tid;
+      const int v = i < nb ? in[i] : 0;
+      int total;
+      const int ex = block_exclusive_scan(v, tmp, &total);
+      if (i < nb) outp[i] = carry + ex;
+      carry += total;
     }
-    __syncthreads();
-    int acc = part[tid];
-    for (int i = hi - 1; i >= lo; --i) { outp[i] = acc; acc += in[i]; }
     __syncthreads();
   }
   for (int s = tid; s < a.n_seq; s += 1024) {

@@ -52,6 +52,26 @@ class HipEvents:
         return ms.value
 
 
+def recorded_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic_*.md), or None when none was taken for the
+    current kernel source."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "attention_qk_norm_amd", "csrc", source)
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
+        text = open(f).read()
+        if "```json" not in text:
+            continue
+        block = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        rec = block.get(kernel)
+        if rec and rec.get("source_sha256_16") == sha:
+            return {"bytes": int(rec["read_bytes"]) + int(rec["write_bytes"]), "read_bytes": int(rec["read_bytes"]),
+                    "write_bytes": int(rec["write_bytes"]), "from": os.path.relpath(f, ROOT)}
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -123,9 +143,10 @@ def run_decode(st):
              out=st["out"], workspace=st["ws"])
 
 
-def cpu_baseline_prefill(spec):
+def cpu_baseline_prefill(spec, n_sample=3):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
-    all query heads of 192 seeded rows of sequence 0 (keys regenerated)."""
+    the first `n_sample` whole sequences of the packed batch (all query heads,
+    every causal row), about 10-15 s of host work."""
     import oracle
     from attention_qk_norm_amd import accounting, inputs
     try:
@@ -133,22 +154,23 @@ def cpu_baseline_prefill(spec):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = None
-    rng = np.random.default_rng(11)
-    L = spec.lengths[0]
-    rows = np.sort(rng.choice(L, size=min(192, L), replace=False))
-    q = np.concatenate([inputs.prefill_seq_rows(spec, 0, r, r + 1, "q") for r in rows])
-    k = inputs.prefill_seq_rows(spec, 0, 0, int(rows.max()) + 1, "k")
-    v = inputs.prefill_seq_rows(spec, 0, 0, int(rows.max()) + 1, "v")
+    n = min(n_sample, spec.n_seq)
     gq, gk = inputs.gammas(spec)
-    t0 = time.perf_counter()
-    oracle.attention_prefill_rows(q, k, v, gq, gk, rows, range(spec.n_q_heads), spec.n_q_heads,
-                                  spec.n_kv_heads, eps=spec.eps, theta=spec.theta)
-    dt = time.perf_counter() - t0
-    flops = 4 * 128 * spec.n_q_heads * int((rows + 1).sum())
+    dt, flops = 0.0, 0
+    for sq in range(n):
+        L = spec.lengths[sq]
+        q = inputs.prefill_seq_rows(spec, sq, 0, L, "q")
+        k = inputs.prefill_seq_rows(spec, sq, 0, L, "k")
+        v = inputs.prefill_seq_rows(spec, sq, 0, L, "v")
+        t0 = time.perf_counter()
+        oracle.attention_prefill(q, k, v, gq, gk, [0, L], spec.n_q_heads, spec.n_kv_heads,
+                                 eps=spec.eps, theta=spec.theta)
+        dt += time.perf_counter() - t0
+        flops += accounting.prefill_flops([L], spec.n_q_heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(), "blas_threads": blas_threads,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"all {spec.n_q_heads} query heads of {len(rows)} seeded rows of sequence 0 "
-                      f"(numpy float64 oracle; algorithmic causal flops of those rows)"}
+            "sample": f"the first {n} sequences of the batch ({n} x {spec.lengths[0]} tokens, all "
+                      f"{spec.n_q_heads} query heads): numpy float64 oracle, algorithmic causal flops"}
 
 
 def main():
@@ -160,6 +182,8 @@ def main():
     ap.add_argument("--decode-case", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention core shards by KV head or sequence with no "
@@ -223,7 +247,8 @@ def main():
         "prefill_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip") if args.prefill_case == 1 else None,
                      "kernel_ms": round(attn_ms, 4), "algorithmic_flops": flops},
     }
     if dec is not None:
@@ -239,8 +264,17 @@ def main():
             "roofline": {"kernel": "k_decode_split", "bound": "hbm",
                          "achieved": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel_ms": round(split_ms, 4)},
+                         "traffic": recorded_traffic("k_decode_split", "k_decode.hip") if args.decode_case == 2 else None,
+                         "kernel_ms": round(split_ms, 4)},
         }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline_prefill(spec)

@@ -84,7 +84,7 @@ def test_bad_lengths_pointers_workspace(lib):
     d2 = B.CacheDesc(8 * 8 * 130, 8 * 130, 130, 8)                     # rows not 16-byte aligned
     assert prefill(lib, p, cu(0, 5), 1, cache=(F, F, d2)) == B.ERR_INVALID_ARG
     assert prefill(lib, p, cu(0), 0) == B.OK                           # n_seq = 0: no-op
-    assert prefill(lib, B.make_params(256, 1), cu(0, 5), 1) == B.ERR_UNSUPPORTED
+    assert prefill(lib, B.make_params(512, 1), cu(0, 5), 1) == B.ERR_UNSUPPORTED  # g > 256
 
 
 def test_decode_capacity_overflow_rejected(lib):
