@@ -27,21 +27,29 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src, objdir):
+# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
+# arch VGPRs: its softmax reads every score with VALU, and the AGPR form made
+# the compiler shuttle the query fragments and scores between register files.
+SOURCE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def _compile(src, objdir, extra=()):
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + list(SOURCE_FLAGS.get(src, ())) + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     return obj, r.returncode, "\n".join(msgs)
 
 
-def build(verbose=False):
-    objdir = os.path.join(PKG, "_build")
+def build(verbose=False, out=None, extra_flags=None):
+    """Compile and link; `out` / `extra_flags` ({source: [flags]}) build variants."""
+    objdir = os.path.join(PKG, "_build" if out is None else "_build_variant")
     os.makedirs(objdir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
+    extra_flags = extra_flags or {}
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        results = list(ex.map(lambda s: _compile(s, objdir), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, objdir, extra_flags.get(s, ())), SOURCES))
     failed = False
     for (obj, rc, msg), src in zip(results, SOURCES):
         if msg.strip() and (verbose or rc):
@@ -49,13 +57,14 @@ def build(verbose=False):
         failed |= rc != 0
     if failed:
         raise RuntimeError("libqwattn: compilation failed")
-    tmp = LIB + ".tmp"
+    lib = LIB if out is None else out
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError("libqwattn: link failed\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -325,7 +325,91 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     }
   };
 
+  // Static-bound tile, software-pipelined at 32-key granularity.  With the
+  // bound there is no row maximum, so the probabilities of keys 0..31 can be
+  // formed while the MFMAs of keys 32..63 run, and those of keys 32..63 while
+  // the PV MFMAs of keys 0..31 run:
+  //   S(keys 0-31) | S(keys 32-63) + exp(0-31) | PV(0-31) + exp(32-63) | PV(32-63)
+  // sched_group_barrier asks the scheduler to interleave each MFMA group with
+  // the VALU work of the same phase.
+  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag) __attribute__((always_inline)) {
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    f32x16 sacc[2][2];  // [key block kb][query block qb]
+    bf16x8 pf[2][4];
+    float psum[2] = {0.f, 0.f};
+    auto s_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[kb][qb][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], sacc[kb][qb], 0, 0, 0);
+      }
+    };
+    // probabilities of key block kb -> P^T fragments kk = 2kb, 2kb+1
+    auto p_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if constexpr (kDiag) {  // key0 + 32kb + 8(j/4) + 4hg + j%4 > qpos  <=>  constant > lim
+          const int lim = qpos[qb] - key0 - 4 * hg - 32 * kb;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (8 * (j >> 2) + (j & 3) > lim) sacc[kb][qb][j] = -INFINITY;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 w4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h + 2 * e], c_log2, -bound[qb]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h + 2 * e + 1], c_log2, -bound[qb]));
+            w4[e] = pack_bf16x2(p0, p1);
+            psum[qb] += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+          }
+          pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w4);
+        }
+      }
+    };
+    auto pv_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = 2 * kb + h;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const lds_u8* vp = vs + v_base + kk * 256 + db * 64;
+          const bf16x8 va = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][kk], o[qb][db], 0, 0, 0);
+        }
+      }
+    };
+    s_block(0);
+    s_block(1);
+    p_block(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of S(keys 32-63)
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // some of the exp(keys 0-31) work
+    }
+    pv_block(0);
+    p_block(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA of PV(keys 0-31)
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // some of the exp(keys 32-63) work
+    }
+    pv_block(1);
+    l_run[0] += psum[0];
+    l_run[1] += psum[1];
+  };
+
   auto run = [&](auto static_tag) __attribute__((always_inline)) {
+    constexpr bool kStatic = decltype(static_tag)::value;
     issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
       const int stage = t & 1;
@@ -335,7 +419,14 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
       const int key0 = t * kTileKeys;
       if (key0 > wave_max) continue;        // every key of the tile is in this wave's future
       const lds_u8* ks = lds + stage * kStageBytes;
-      tile(ks, ks + kKTile, key0, static_tag);
+      if constexpr (kStatic) {
+        if (key0 + kTileKeys - 1 > wave_min)
+          static_tile(ks, ks + kKTile, key0, std::true_type{});
+        else
+          static_tile(ks, ks + kKTile, key0, std::false_type{});
+      } else {
+        tile(ks, ks + kKTile, key0, static_tag);
+      }
     }
   };
   if (use_static)
