@@ -110,6 +110,12 @@ __device__ __forceinline__ float pair_max(float x) {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
+// acc + lo + hi of a packed bf16 pair, in one v_dot2c_f32_bf16 against (1, 1).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
+                                         false);
+}
+
 // gfx950 transposed LDS read: within each 16-lane group, lane i receives
 // element (i % 4) of the 8 bytes that lanes 4r + i/4 (r = 0..3) point at, as
 // its elements r = 0..3.  Returned as two dwords.

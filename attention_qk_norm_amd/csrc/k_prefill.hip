@@ -25,14 +25,19 @@
 // K/V tiles of 64 keys go HBM -> LDS directly (global_load_lds_dwordx4, no
 // staging registers) into a two-stage ring: tile t+1 lands while tile t is used.
 //
-// Softmax: QK-Norm bounds every logit.  With q^ the bf16 query row and every
-// rotated key of norm <= sqrt(128) max|gamma_k| (RoPE keeps norms), the scaled
-// score is at most B = scale * |q^| * sqrt(128) * max|gamma_k| (plus a margin
-// for bf16 rounding).  p = 2^(s log2e - B) then needs no running max and no
-// rescaling of the accumulators, and stays a normal float as long as B <= 60
-// (in log2 units).  A wave with any larger bound runs the usual online softmax.
-// Both are exactly softmax; only rounding differs.  Tiles entirely above a
-// wave's diagonal are skipped; only tiles crossing it are masked.
+// Softmax: QK-Norm bounds every logit.  The query rows are pre-multiplied by
+// c = scale * log2(e) before their bf16 rounding, so the MFMA scores are in
+// log2 units, and |score| <= c * 128 * max|gamma_q| * max|gamma_k| (query rows
+// have norm <= sqrt(128) max|gamma_q|, rotated keys <= sqrt(128) max|gamma_k|,
+// RoPE keeps norms; a small margin covers the bf16 roundings).  When that bound
+// is <= 60, p = 2^score is a normal float for every key (in fp32 and in bf16),
+// so softmax needs no running maximum, no rescaling and no subtraction: the
+// weights are exp2 of the accumulators, and the tile pipelines at 32-key
+// granularity.  Otherwise the kernel runs the usual online softmax.  Both are
+// exactly softmax; only rounding differs.  The row sum adds the bf16-rounded
+// weights the PV MFMA uses, so every output row is an exact convex combination
+// of V rows.  Tiles entirely above a wave's diagonal are skipped; only tiles
+// crossing it are masked.
 #include <type_traits>
 
 #include "kernels.h"
@@ -107,10 +112,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   // Lane (n, hg) holds dims 16kk + 8hg + e (kk < 8, e < 8); dims i and i + 64 of
   // a rotation pair sit in fragments kk and kk + 4 of the same lane.
   bf16x8 qf[2][8];
-  float bound[2];
-  // max |gamma| of q and k: every rotated query row then has norm <=
-  // sqrt(128) max|gamma_q| and every key <= sqrt(128) max|gamma_k|, which bounds
-  // all logits of the launch by the same number in every wave.
+  // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
+  // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
+  // norms), so |logit| * log2(e) <= c * 128 * max|gamma_q| * max|gamma_k| with
+  // c = scale * log2(e), plus a margin for the bf16 roundings.
   float kmax, qmax;
   {
     const uint16_t* gk = (const uint16_t*)a.k_gamma;
@@ -123,11 +128,11 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
       qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
     }
   }
-  const float bound_scale = a.scale_log2e * 11.313708498984761f * kmax * (1.0f + 1.0f / 128);
-  const bool use_static = bound_scale * 11.313708498984761f * qmax * (1.0f + 1.0f / 128) <= kStaticBoundMax;
-  // QK-Norm + RoPE of one query row into bf16 fragments; returns the row's logit
-  // bound.  Called once per query block with static arguments, so the fragment
-  // arrays stay in registers.
+  const float c_log2 = a.scale_log2e;
+  const bool use_static = c_log2 * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+  // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
+  // scores come out in log2 units), into bf16 fragments.  Called once per query
+  // block with static arguments, so the fragment arrays stay in registers.
   auto row_prologue = [&](bool ok, int tok, int head, bf16x8 (&frag)[8]) __attribute__((always_inline)) {
     float x[8][8];
     if (ok) {
@@ -176,23 +181,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk + 4][e] = y2 * c + y1 * sn;
       }
     }
-    float qn = 0.f;  // squared norm of the bf16 row that the MFMAs will see
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       u32x4 w4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w4[e] = pack_bf16x2(x[kk][2 * e], x[kk][2 * e + 1]);
-        const float f0 = bf16_lo(w4[e]), f1 = bf16_hi(w4[e]);
-        qn += f0 * f0 + f1 * f1;
-      }
+      for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(x[kk][2 * e] * c_log2, x[kk][2 * e + 1] * c_log2);
       frag[kk] = __builtin_bit_cast(bf16x8, w4);
     }
-    return sqrtf(pair_sum(qn)) * bound_scale;
   };
-  bound[0] = row_prologue(valid[0], qtok[0], t_head[0], qf[0]);
+  row_prologue(valid[0], qtok[0], t_head[0], qf[0]);
   __builtin_amdgcn_sched_barrier(0);
-  bound[1] = row_prologue(valid[1], qtok[1], t_head[1], qf[1]);
+  row_prologue(valid[1], qtok[1], t_head[1], qf[1]);
 
   // ---- K/V sources for (sequence s, KV head u)
   const uint16_t* kbase = (const uint16_t*)a.khat + u * a.ks_head +
@@ -200,19 +199,35 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const uint16_t* vbase = (const uint16_t*)a.v + u * a.vs_head +
                           (a.v_packed ? (int64_t)seq0 * a.vs_tok : (int64_t)s * a.vs_seq);
 
-  // Each wave fills blocks 4w .. 4w+3 of K and of V per tile.  Keys past n_kv
-  // repeat the last key: they are masked, and stay finite.
+  // Each wave fills blocks 4w .. 4w+3 of K and of V per tile.  A lane's byte
+  // offset inside a tile is fixed; the tile base is uniform (scalar).  Keys
+  // past n_kv (last tile only) repeat the last key: they are masked, and stay
+  // finite.
+  const int64_t kstride = a.ks_tok * 2, vstride = a.vs_tok * 2;  // bytes per key row
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = (w * 4 + m) + 16 * (lane >> 4);
+    koff[m] = (uint32_t)(row * kstride) + (lane & 15) * 16;
+    voff[m] = (uint32_t)(row * vstride) + (lane & 15) * 16;
+  }
   auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
     lds_u8* kdst = lds + stage * kStageBytes;
     lds_u8* vdst = kdst + kKTile;
+    const char* kt = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
+    const char* vt = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
+    const bool tail = (t + 1) * kTileKeys > n_kv;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int blk = w * 4 + m;
-      const int row = blk + 16 * (lane >> 4);
-      const int col = (lane & 15) * 8;
-      const int key = min(t * kTileKeys + row, n_kv - 1);
-      load_lds16(kbase + (int64_t)key * a.ks_tok + col, kdst + blk * kKBlk);
-      load_lds16(vbase + (int64_t)key * a.vs_tok + col, vdst + blk * kVBlk);
+      uint32_t ko = koff[m], vo = voff[m];
+      if (tail) {
+        const int r = min(blk + 16 * (lane >> 4), n_kv - 1 - t * kTileKeys);
+        ko = (uint32_t)(r * kstride) + (lane & 15) * 16;
+        vo = (uint32_t)(r * vstride) + (lane & 15) * 16;
+      }
+      load_lds16(kt + ko, kdst + blk * kKBlk);
+      load_lds16(vt + vo, vdst + blk * kVBlk);
     }
   };
 
@@ -235,11 +250,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const int v_base = v_row0 * kVBlk + v_col0 * 2;
 
   const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
-  const float c_log2 = a.scale_log2e;
 
-  // One tile: S^T = K Q^T, softmax in place on the accumulators, O^T += V^T P^T.
-  auto tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto static_tag) __attribute__((always_inline)) {
-    constexpr bool kStatic = decltype(static_tag)::value;
+  // One tile with the online softmax (running max, rescaled accumulators):
+  // S^T = K Q^T, softmax in place on the accumulators, O^T += V^T P^T.
+  auto tile = [&](const lds_u8* ks, const lds_u8* vs, int key0) __attribute__((always_inline)) {
     f32x16 sacc[2][2];  // [key block kb][query block qb]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -271,15 +285,13 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
             if (32 * kb + 8 * (j >> 2) + (j & 3) > lim) sacc[kb][qb][j] = -INFINITY;
       }
       float m_use;
-      if constexpr (kStatic) {
-        m_use = bound[qb];
-      } else {
+      {
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[kb][qb][j]);
-        mt = pair_max(mt) * c_log2;
+        mt = pair_max(mt);
         const float m_new = fmaxf(m_run[qb], mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          sacc[kb][qb][j] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][j], c_log2, -m_use));
+          sacc[kb][qb][j] = __builtin_amdgcn_exp2f(sacc[kb][qb][j] - m_use);
       // P^T fragments: slice kk (16 keys) = registers 8(kk%2) .. +7 of block kk/2.
       // The row sum adds the bf16-rounded weights the MFMA uses, so every output
       // row is an exact convex combination of V rows.
@@ -305,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           w4[e] = pack_bf16x2(sacc[kk >> 1][qb][8 * (kk & 1) + 2 * e], sacc[kk >> 1][qb][8 * (kk & 1) + 2 * e + 1]);
-          psum += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+          psum = sum_bf16x2(w4[e], psum);
         }
         pf[qb][kk] = __builtin_bit_cast(bf16x8, w4);
       }
@@ -339,15 +351,11 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     float psum[2] = {0.f, 0.f};
     auto s_block = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[kb][qb][j] = 0.f;
-#pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], sacc[kb][qb], 0, 0, 0);
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], kk == 0 ? f32x16{} : sacc[kb][qb], 0, 0, 0);
       }
     };
     // probabilities of key block kb -> P^T fragments kk = 2kb, 2kb+1
@@ -365,10 +373,9 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
           u32x4 w4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h + 2 * e], c_log2, -bound[qb]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * h + 2 * e + 1], c_log2, -bound[qb]));
-            w4[e] = pack_bf16x2(p0, p1);
-            psum[qb] += bf16_lo(w4[e]) + bf16_hi(w4[e]);
+            w4[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[kb][qb][8 * h + 2 * e]),
+                                __builtin_amdgcn_exp2f(sacc[kb][qb][8 * h + 2 * e + 1]));
+            psum[qb] = sum_bf16x2(w4[e], psum[qb]);
           }
           pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w4);
         }
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         else
           static_tile(ks, ks + kKTile, key0, std::false_type{});
       } else {
-        tile(ks, ks + kKTile, key0, static_tag);
+        tile(ks, ks + kKTile, key0);
       }
     }
   };
