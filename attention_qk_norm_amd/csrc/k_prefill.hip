@@ -23,7 +23,8 @@
 // ds_read_b64_tr_b16 (two per fragment).
 //
 // K/V tiles of 64 keys go HBM -> LDS directly (global_load_lds_dwordx4, no
-// staging registers) into a two-stage ring: tile t+1 lands while tile t is used.
+// staging registers) into a three-stage ring: tiles t+1 and t+2 land while tile
+// t is used.
 //
 // Softmax: QK-Norm bounds every logit.  The query rows are pre-multiplied by
 // c = scale * log2(e) before their bf16 rounding, so the MFMA scores are in
@@ -60,18 +61,29 @@ constexpr float kStaticBoundMax = 60.f;             // log2 units
 constexpr int kKBlk = 1040, kVBlk = 1088;
 constexpr int kKTile = 16 * kKBlk, kVTile = 16 * kVBlk;
 constexpr int kStageBytes = kKTile + kVTile;
+// Three-stage ring: tile t is read while tiles t+1 and t+2 are in flight.
+constexpr int kStages = 3;
+constexpr int kLoadsPerTile = 8;  // direct loads per lane per tile (4 K blocks, 4 V blocks)
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
 }
 
-__device__ __forceinline__ void load_lds16(const void* g, lds_u8* l) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes, read from
+// gbase + voff, land at LDS address lds_base + 16 l (M0 holds the wave-uniform
+// base; one wait state after writing M0).  Written as inline assembly so the
+// compiler does not put a wait for every outstanding copy in front of each LDS
+// read: the tile loop waits for its own copies (s_waitcnt vmcnt) before the
+// barrier that publishes a tile.
+__device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
 }
 
 __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 2 stages x (K, V)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kStages x (K, V)
   lds_u8* lds = (lds_u8*)(smem);
 
   const int tid = threadIdx.x;
@@ -211,23 +223,25 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     koff[m] = (uint32_t)(row * kstride) + (lane & 15) * 16;
     voff[m] = (uint32_t)(row * vstride) + (lane & 15) * 16;
   }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
-    lds_u8* kdst = lds + stage * kStageBytes;
-    lds_u8* vdst = kdst + kKTile;
+    const uint32_t kdst = lds0 + stage * kStageBytes;
+    const uint32_t vdst = kdst + kKTile;
     const char* kt = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
     const char* vt = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
     const bool tail = (t + 1) * kTileKeys > n_kv;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int blk = w * 4 + m;
+      const int blk = wu * 4 + m;
       uint32_t ko = koff[m], vo = voff[m];
       if (tail) {
-        const int r = min(blk + 16 * (lane >> 4), n_kv - 1 - t * kTileKeys);
+        const int r = min(w * 4 + m + 16 * (lane >> 4), n_kv - 1 - t * kTileKeys);
         ko = (uint32_t)(r * kstride) + (lane & 15) * 16;
         vo = (uint32_t)(r * vstride) + (lane & 15) * 16;
       }
-      load_lds16(kt + ko, kdst + blk * kKBlk);
-      load_lds16(vt + vo, vdst + blk * kVBlk);
+      load_lds16_async(kdst + blk * kKBlk, kt, ko);
+      load_lds16_async(vdst + blk * kVBlk, vt, vo);
     }
   };
 
@@ -418,11 +432,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   auto run = [&](auto static_tag) __attribute__((always_inline)) {
     constexpr bool kStatic = decltype(static_tag)::value;
     issue_tile(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
-      const int stage = t & 1;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's part of tile t is in LDS
-      __syncthreads();                      // ... everyone's, and tile t-1's stage is free
-      if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
+    if (n_tiles > 1) issue_tile(1, 1);
+    int stage = 0;
+    for (int t = 0; t < n_tiles; ++t, stage = stage == kStages - 1 ? 0 : stage + 1) {
+      // This thread's part of tile t is in LDS once at most tile t+1's copies
+      // are outstanding; the barrier then publishes everyone's part and frees
+      // the stage of tile t-1, which receives tile t+2.
+      static_assert(kLoadsPerTile == 8, "vmcnt immediate below");
+      if (t + 1 < n_tiles)
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (t + 2 < n_tiles) issue_tile(t + 2, stage == 0 ? 2 : stage - 1);
       const int key0 = t * kTileKeys;
       if (key0 > wave_max) continue;        // every key of the tile is in this wave's future
       const lds_u8* ks = lds + stage * kStageBytes;
@@ -529,10 +551,10 @@ hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+      hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kStages * kStageBytes);
   if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), 2 * kStageBytes, st, a);
+  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), kStages * kStageBytes, st, a);
   return hipGetLastError();
 }
 
