@@ -351,80 +351,98 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     }
   };
 
-  // Static-bound tile, software-pipelined at 32-key granularity.  With the
-  // bound there is no row maximum, so the probabilities of keys 0..31 can be
-  // formed while the MFMAs of keys 32..63 run, and those of keys 32..63 while
-  // the PV MFMAs of keys 0..31 run:
+  // Static-bound tile, software-pipelined at 32-key granularity and issued in
+  // a fixed order.  With the bound there is no row maximum, so the weights of
+  // keys 0..31 are formed while the S MFMAs of keys 32..63 run, and those of
+  // keys 32..63 while the PV MFMAs of keys 0..31 run:
   //   S(keys 0-31) | S(keys 32-63) + exp(0-31) | PV(0-31) + exp(32-63) | PV(32-63)
-  // sched_group_barrier asks the scheduler to interleave each MFMA group with
-  // the VALU work of the same phase.
+  // One wave per SIMD issues in order, so the order is the schedule: every MFMA
+  // is followed by a quarter of one weight group (two keys) for the VALU to
+  // run under it, and every step issues the LDS fragment read that is needed
+  // three steps later.  sched_barrier keeps the compiler from regrouping them.
   auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag) __attribute__((always_inline)) {
     constexpr bool kDiag = decltype(diag_tag)::value;
     f32x16 sacc[2][2];  // [key block kb][query block qb]
-    bf16x8 pf[2][4];
+    bf16x8 pf[2][4];    // [qb][16-key slice kk]
+    u32x4 w4[2][2][2];  // [kb][qb][h]: weights being packed into pf[qb][2kb + h]
     float psum[2] = {0.f, 0.f};
-    auto s_block = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][kk], kk == 0 ? f32x16{} : sacc[kb][qb], 0, 0, 0);
-      }
+    bf16x8 kf[16];      // K fragment (kb, kk) at 8kb + kk
+    bf16x8 vf[16];      // V fragment (kk, db) at 4kk + db
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      kf[i] = lds_load_b128(ks + k_base + (i >> 3) * 512 + (i & 7) * 32);
     };
-    // probabilities of key block kb -> P^T fragments kk = 2kb, 2kb+1
-    auto p_block = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if constexpr (kDiag) {  // key0 + 32kb + 8(j/4) + 4hg + j%4 > qpos  <=>  constant > lim
-          const int lim = qpos[qb] - key0 - 4 * hg - 32 * kb;
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (8 * (j >> 2) + (j & 3) > lim) sacc[kb][qb][j] = -INFINITY;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 w4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w4[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sacc[kb][qb][8 * h + 2 * e]),
-                                __builtin_amdgcn_exp2f(sacc[kb][qb][8 * h + 2 * e + 1]));
-            psum[qb] = sum_bf16x2(w4[e], psum[qb]);
-          }
-          pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w4);
-        }
-      }
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const lds_u8* vp = vs + v_base + (i >> 2) * 256 + (i & 3) * 64;
+      vf[i] = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
     };
-    auto pv_block = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kk = 2 * kb + h;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const lds_u8* vp = vs + v_base + kk * 256 + db * 64;
-          const bf16x8 va = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[qb][kk], o[qb][db], 0, 0, 0);
-        }
-      }
+    auto smfma = [&](int kb, int kk, int qb) __attribute__((always_inline)) {
+      sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[8 * kb + kk], qf[qb][kk],
+                                                             kk == 0 ? f32x16{} : sacc[kb][qb], 0, 0, 0);
     };
-    s_block(0);
-    s_block(1);
-    p_block(0);
+    auto pmfma = [&](int i, int qb) __attribute__((always_inline)) {
+      o[qb][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[qb][i >> 2], o[qb][i & 3], 0, 0, 0);
+    };
+    // Weight pair m (0..15) of key block kb: query block m / 8, registers
+    // j = 2(m % 8), +1 of sacc[kb][qb], i.e. keys key0 + 32kb + 8(j/4) + 4hg + j%4.
+    auto weights = [&](int kb, int m) __attribute__((always_inline)) {
+      const int qb = m >> 3, j = 2 * (m & 7), h = j >> 3, e = (j & 7) >> 1;
+      float x0 = sacc[kb][qb][j], x1 = sacc[kb][qb][j + 1];
+      if constexpr (kDiag) {  // key > qpos  <=>  constant > lim
+        const int lim = qpos[qb] - key0 - 4 * hg - 32 * kb;
+        if (8 * (j >> 2) + (j & 3) > lim) x0 = -INFINITY;
+        if (8 * ((j + 1) >> 2) + ((j + 1) & 3) > lim) x1 = -INFINITY;
+      }
+      w4[kb][qb][h][e] = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+      psum[qb] = sum_bf16x2(w4[kb][qb][h][e], psum[qb]);
+      if (e == 3) pf[qb][2 * kb + h] = __builtin_bit_cast(bf16x8, w4[kb][qb][h]);
+    };
+
+    kread(0);
+    kread(1);
+    kread(2);
+    fence();
+    // S(keys 0-31); the reads run ahead into the K fragments of keys 32-63
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA of S(keys 32-63)
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // some of the exp(keys 0-31) work
+    for (int kk = 0; kk < 8; ++kk) {
+      smfma(0, kk, 0);
+      smfma(0, kk, 1);
+      kread(kk + 3);
+      fence();
     }
-    pv_block(0);
-    p_block(1);
+    // S(keys 32-63) + weights of keys 0-31; then the first V fragments
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA of PV(keys 0-31)
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // some of the exp(keys 32-63) work
+    for (int kk = 0; kk < 8; ++kk) {
+      smfma(1, kk, 0);
+      weights(0, 2 * kk);
+      fence();
+      smfma(1, kk, 1);
+      weights(0, 2 * kk + 1);
+      if (kk < 5)
+        kread(8 + kk + 3);
+      else
+        vread(kk - 5);
+      fence();
     }
-    pv_block(1);
+    // PV(keys 0-31) + weights of keys 32-63
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pmfma(i, 0);
+      weights(1, 2 * i);
+      fence();
+      pmfma(i, 1);
+      weights(1, 2 * i + 1);
+      vread(i + 3);
+      fence();
+    }
+    // PV(keys 32-63)
+#pragma unroll
+    for (int i = 8; i < 16; ++i) {
+      pmfma(i, 0);
+      pmfma(i, 1);
+      if (i + 3 < 16) vread(i + 3);
+      fence();
+    }
     l_run[0] += psum[0];
     l_run[1] += psum[1];
   };
