@@ -64,6 +64,13 @@ constexpr int kStageBytes = kKTile + kVTile;
 // Three-stage ring: tile t is read while tiles t+1 and t+2 are in flight.
 constexpr int kStages = 3;
 constexpr int kLoadsPerTile = 8;  // direct loads per lane per tile (4 K blocks, 4 V blocks)
+constexpr int kRopeRow = kHalf + 2;  // float2 entries per row of the cos/sin table (16 B pad)
+// Dynamic LDS: the K/V ring, or the prologue's cos/sin table if that is larger
+// (bm_tok = 256 / g tokens; at most 256).
+constexpr int kPrefillSmemMax = kPrefillRows * kRopeRow * 8 > kStages * kStageBytes ? kPrefillRows * kRopeRow * 8
+                                                                                  : kStages * kStageBytes;
+static_assert(kPrefillSmemMax <= 160 * 1024, "LDS per workgroup");
+inline int prefill_smem_bytes(int bm_tok) { return bm_tok * kRopeRow * 8 > kStages * kStageBytes ? bm_tok * kRopeRow * 8 : kStages * kStageBytes; }
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
@@ -145,6 +152,20 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
   // scores come out in log2 units), into bf16 fragments.  Called once per query
   // block with static arguments, so the fragment arrays stay in registers.
+  // cos/sin of the workgroup's bm_tok positions (tok_base ..) at the 64 RoPE
+  // angles, tabulated once in LDS (the K/V stages are not in use yet) and
+  // shared by the g heads of each token.  Rows are padded by 16 bytes so the
+  // 16 lanes of a b128 read pass hit distinct banks.
+  float2* const rope_t = (float2*)smem;
+  {
+    const double wi = a.rope.w[tid & (kHalf - 1)];  // 256 is a multiple of 64: one angle index per thread
+    for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
+      float c, sn;
+      rope_cos_sin(tok_base + (e >> 6), wi, c, sn);
+      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] = make_float2(c, sn);
+    }
+  }
+  __syncthreads();
   auto row_prologue = [&](bool ok, int tok, int head, bf16x8 (&frag)[8]) __attribute__((always_inline)) {
     float x[8][8];
     if (ok) {
@@ -181,16 +202,15 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk][2 * e + 1] *= inv * bf16_hi(gr[e]);
       }
     }
-    const int p = ok ? tok : 0;
+    const float2* cs = rope_t + (ok ? tok - tok_base : 0) * kRopeRow + 8 * hg;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float c, sn;
-        rope_cos_sin(p, a.rope.w[16 * kk + 8 * hg + e], c, sn);
+        const float2 v = cs[16 * kk + e];
         const float y1 = x[kk][e], y2 = x[kk + 4][e];
-        x[kk][e] = y1 * c - y2 * sn;
-        x[kk + 4][e] = y2 * c + y1 * sn;
+        x[kk][e] = y1 * v.x - y2 * v.y;
+        x[kk + 4][e] = y2 * v.x + y1 * v.y;
       }
     }
 #pragma unroll
@@ -204,6 +224,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   row_prologue(valid[0], qtok[0], t_head[0], qf[0]);
   __builtin_amdgcn_sched_barrier(0);
   row_prologue(valid[1], qtok[1], t_head[1], qf[1]);
+  __syncthreads();  // every wave is done with the table before tiles land on it
 
   // ---- K/V sources for (sequence s, KV head u)
   const uint16_t* kbase = (const uint16_t*)a.khat + u * a.ks_head +
@@ -569,10 +590,10 @@ hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kStages * kStageBytes);
+      hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillSmemMax);
   if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), kStages * kStageBytes, st, a);
+  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), prefill_smem_bytes(a.bm_tok), st, a);
   return hipGetLastError();
 }
 
