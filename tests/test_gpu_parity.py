@@ -194,6 +194,35 @@ def test_prefill_empty_and_zero_length():
               torch.zeros(1, dtype=torch.int32, device=U.DEV), [0])
 
 
+def test_prefill_online_softmax_path():
+    """One large gamma entry each in q and k lifts the launch-wide QK-Norm
+    logit bound, scale * log2(e) * 128 * max|gamma_q| * max|gamma_k| (+1/64),
+    above 60 in log2 units, so the bf16 kernel runs its online (running-max)
+    softmax instead of the static-bound one, while typical logits stay the
+    configs' size (scaling every gamma instead sharpens the softmax until bf16
+    operands alone exceed the tolerance).  Same tolerance as every bf16 case;
+    the first row of each sequence is still exactly v_0."""
+    spec = inputs.custom_spec(122, "bf16", 8, 2, [1, 64, 65, 200, 517])
+    x = dict(inputs.prefill_inputs(spec))
+    x["q_gamma"] = x["q_gamma"].copy()
+    x["k_gamma"] = x["k_gamma"].copy()
+    x["q_gamma"][5] = 3.5
+    x["k_gamma"][70] = -3.0
+    bound = (1.0 / np.sqrt(128.0)) * np.log2(np.e) * 128.0 * np.abs(x["q_gamma"]).max() * \
+        np.abs(x["k_gamma"]).max() * (1.0 + 1.0 / 64)
+    assert bound > 60.0, bound
+    U.say(f"prefill online-softmax path (logit bound {bound:.1f} in log2 units)")
+    out_t = U.run_prefill(spec, x)
+    out = U.down(out_t)
+    ref = oracle.attention_prefill(x["q"], x["k"], x["v"], x["q_gamma"], x["k_gamma"], x["cu_seqlens"], 8, 2,
+                                   eps=spec.eps, theta=spec.theta)
+    print(U.bf16_gate(out, ref, spec, label="online path"))
+    cu = x["cu_seqlens"]
+    for s in range(len(spec.lengths)):
+        for t in range(8):
+            assert torch.equal(out_t[cu[s], t], U.up(x["v"][cu[s], t // 4], torch.bfloat16))
+
+
 @pytest.mark.parametrize("case_id", [1, 3, 4])
 def test_prefill_full_size_sampled(case_id):
     """Full-size standard workloads in the benchmark's launch configuration;
