@@ -213,11 +213,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk + 4][e] = y2 * v.x + y1 * v.y;
       }
     }
+    // The fragments are only ever MFMA B operands, which gfx950 reads from
+    // AGPRs directly: writing them there keeps the 64 registers out of the
+    // VGPR file that the tile loop fills with scores, weights and O.
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       u32x4 w4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(x[kk][2 * e] * c_log2, x[kk][2 * e + 1] * c_log2);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = pack_bf16x2(x[kk][2 * e] * c_log2, x[kk][2 * e + 1] * c_log2);
+        asm("v_accvgpr_write_b32 %0, %1" : "=a"(w4[e]) : "v"(v));
+      }
       frag[kk] = __builtin_bit_cast(bf16x8, w4);
     }
   };
