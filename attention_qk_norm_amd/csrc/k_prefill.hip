@@ -127,111 +127,6 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     wave_max = max(wave_max, __shfl_xor(wave_max, m, 64));
   }
 
-  // ---- prologue: QK-Norm + RoPE of each query row, kept as bf16 MFMA fragments.
-  // Lane (n, hg) holds dims 16kk + 8hg + e (kk < 8, e < 8); dims i and i + 64 of
-  // a rotation pair sit in fragments kk and kk + 4 of the same lane.
-  bf16x8 qf[2][8];
-  // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
-  // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
-  // norms), so |logit| * log2(e) <= c * 128 * max|gamma_q| * max|gamma_k| with
-  // c = scale * log2(e), plus a margin for the bf16 roundings.
-  float kmax, qmax;
-  {
-    const uint16_t* gk = (const uint16_t*)a.k_gamma;
-    const uint16_t* gq = (const uint16_t*)a.q_gamma;
-    kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * lane])), fabsf(bf16_to_f32(gk[2 * lane + 1])));
-    qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * lane])), fabsf(bf16_to_f32(gq[2 * lane + 1])));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
-      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
-    }
-  }
-  const float c_log2 = a.scale_log2e;
-  const bool use_static = c_log2 * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
-  // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
-  // scores come out in log2 units), into bf16 fragments.  Called once per query
-  // block with static arguments, so the fragment arrays stay in registers.
-  // cos/sin of the workgroup's bm_tok positions (tok_base ..) at the 64 RoPE
-  // angles, tabulated once in LDS (the K/V stages are not in use yet) and
-  // shared by the g heads of each token.  Rows are padded by 16 bytes so the
-  // 16 lanes of a b128 read pass hit distinct banks.
-  float2* const rope_t = (float2*)smem;
-  {
-    const double wi = a.rope.w[tid & (kHalf - 1)];  // 256 is a multiple of 64: one angle index per thread
-    for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
-      float c, sn;
-      rope_cos_sin(tok_base + (e >> 6), wi, c, sn);
-      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] = make_float2(c, sn);
-    }
-  }
-  __syncthreads();
-  auto row_prologue = [&](bool ok, int tok, int head, bf16x8 (&frag)[8]) __attribute__((always_inline)) {
-    float x[8][8];
-    if (ok) {
-      const uint16_t* src = (const uint16_t*)a.q + ((int64_t)(seq0 + tok) * a.Hq + head) * kD + 8 * hg;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * kk);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[kk][2 * e] = bf16_lo(raw[e]);
-          x[kk][2 * e + 1] = bf16_hi(raw[e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[kk][e] = 0.f;
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
-    ss = pair_sum(ss);  // lane l ^ 32 holds the other half of the row
-    const float inv = rsqrtf(ss * (1.0f / kD) + a.eps);
-    const uint16_t* gsrc = (const uint16_t*)a.q_gamma + 8 * hg;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 gr = *reinterpret_cast<const u32x4*>(gsrc + 16 * kk);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[kk][2 * e] *= inv * bf16_lo(gr[e]);
-        x[kk][2 * e + 1] *= inv * bf16_hi(gr[e]);
-      }
-    }
-    const float2* cs = rope_t + (ok ? tok - tok_base : 0) * kRopeRow + 8 * hg;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 v = cs[16 * kk + e];
-        const float y1 = x[kk][e], y2 = x[kk + 4][e];
-        x[kk][e] = y1 * v.x - y2 * v.y;
-        x[kk + 4][e] = y2 * v.x + y1 * v.y;
-      }
-    }
-    // The fragments are only ever MFMA B operands, which gfx950 reads from
-    // AGPRs directly: writing them there keeps the 64 registers out of the
-    // VGPR file that the tile loop fills with scores, weights and O.
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      u32x4 w4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t v = pack_bf16x2(x[kk][2 * e] * c_log2, x[kk][2 * e + 1] * c_log2);
-        asm("v_accvgpr_write_b32 %0, %1" : "=a"(w4[e]) : "v"(v));
-      }
-      frag[kk] = __builtin_bit_cast(bf16x8, w4);
-    }
-  };
-  row_prologue(valid[0], qtok[0], t_head[0], qf[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  row_prologue(valid[1], qtok[1], t_head[1], qf[1]);
-  __syncthreads();  // every wave is done with the table before tiles land on it
-
   // ---- K/V sources for (sequence s, KV head u)
   const uint16_t* kbase = (const uint16_t*)a.khat + u * a.ks_head +
                           (a.k_packed ? (int64_t)seq0 * a.ks_tok : (int64_t)s * a.ks_seq);
@@ -271,6 +166,133 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
       load_lds16_async(vdst + blk * kVBlk, vt, vo);
     }
   };
+  const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
+
+  // ---- prologue: QK-Norm + RoPE of each query row, kept as bf16 MFMA fragments.
+  // Lane (n, hg) holds dims 16kk + 8hg + e (kk < 8, e < 8); dims i and i + 64 of
+  // a rotation pair sit in fragments kk and kk + 4 of the same lane.
+  bf16x8 qf[2][8];
+  // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
+  // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
+  // norms), so |logit| * log2(e) <= c * 128 * max|gamma_q| * max|gamma_k| with
+  // c = scale * log2(e), plus a margin for the bf16 roundings.
+  float kmax, qmax;
+  {
+    const uint16_t* gk = (const uint16_t*)a.k_gamma;
+    const uint16_t* gq = (const uint16_t*)a.q_gamma;
+    kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * lane])), fabsf(bf16_to_f32(gk[2 * lane + 1])));
+    qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * lane])), fabsf(bf16_to_f32(gq[2 * lane + 1])));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
+      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
+    }
+  }
+  const float c_log2 = a.scale_log2e;
+  const bool use_static = c_log2 * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+  // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
+  // scores come out in log2 units), into bf16 fragments.  Called once per query
+  // block with static arguments, so the fragment arrays stay in registers.
+  // cos/sin of the workgroup's bm_tok positions (tok_base ..) at the 64 RoPE
+  // angles, tabulated once in LDS (the K/V stages are not in use yet) and
+  // shared by the g heads of each token.  Rows are padded by 16 bytes so the
+  // 16 lanes of a b128 read pass hit distinct banks.
+  // When the table fits in one ring stage (g >= 4) it goes to stage 2, which
+  // the first tile copies do not touch: tiles 0 and 1 and the query rows are
+  // then already in flight while the table is computed.  (Stage 2 first
+  // receives tile 2, after the loop's first barrier.)
+  const bool early = a.bm_tok * kRopeRow * 8 <= kStageBytes;
+  float2* const rope_t = (float2*)(smem + (early ? 2 * kStageBytes : 0));
+  u32x4 qraw[2][8];  // raw bf16 query rows: dims 16kk + 8hg .. +7
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t* src = (const uint16_t*)a.q + ((int64_t)(seq0 + (valid[qb] ? qtok[qb] : 0)) * a.Hq +
+                                                  (valid[qb] ? t_head[qb] : 0)) * kD + 8 * hg;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qraw[qb][kk] = *reinterpret_cast<const u32x4*>(src + 16 * kk);
+  }
+  u32x4 graw[8];  // gamma_q at the same dims
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) graw[kk] = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q_gamma + 8 * hg + 16 * kk);
+  if (early) {
+    issue_tile(0, 0);
+    if (n_tiles > 1) issue_tile(1, 1);
+  }
+  {
+    const double wi = a.rope.w[tid & (kHalf - 1)];  // 256 is a multiple of 64: one angle index per thread
+    for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
+      float c, sn;
+      rope_cos_sin(tok_base + (e >> 6), wi, c, sn);
+      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] = make_float2(c, sn);
+    }
+  }
+  __syncthreads();
+  auto row_prologue = [&](bool ok, int tok, const u32x4 (&raw)[8], bf16x8 (&frag)[8]) __attribute__((always_inline)) {
+    float x[8][8];
+    if (ok) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[kk][2 * e] = bf16_lo(raw[kk][e]);
+          x[kk][2 * e + 1] = bf16_hi(raw[kk][e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[kk][e] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
+    ss = pair_sum(ss);  // lane l ^ 32 holds the other half of the row
+    const float inv = rsqrtf(ss * (1.0f / kD) + a.eps);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[kk][2 * e] *= inv * bf16_lo(graw[kk][e]);
+        x[kk][2 * e + 1] *= inv * bf16_hi(graw[kk][e]);
+      }
+    }
+    const float2* cs = rope_t + (ok ? tok - tok_base : 0) * kRopeRow + 8 * hg;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 v = cs[16 * kk + e];
+        const float y1 = x[kk][e], y2 = x[kk + 4][e];
+        x[kk][e] = y1 * v.x - y2 * v.y;
+        x[kk + 4][e] = y2 * v.x + y1 * v.y;
+      }
+    }
+    // The fragments are only ever MFMA B operands, which gfx950 reads from
+    // AGPRs directly: writing them there keeps the 64 registers out of the
+    // VGPR file that the tile loop fills with scores, weights and O.
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = pack_bf16x2(x[kk][2 * e] * c_log2, x[kk][2 * e + 1] * c_log2);
+        asm("v_accvgpr_write_b32 %0, %1" : "=a"(w4[e]) : "v"(v));
+      }
+      frag[kk] = __builtin_bit_cast(bf16x8, w4);
+    }
+  };
+  row_prologue(valid[0], qtok[0], qraw[0], qf[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  row_prologue(valid[1], qtok[1], qraw[1], qf[1]);
+  if (!early) {
+    __syncthreads();  // every wave is done with the table before tiles land on it
+    issue_tile(0, 0);
+    if (n_tiles > 1) issue_tile(1, 1);
+  }
+
 
   f32x16 o[2][4];
 #pragma unroll
@@ -290,7 +312,6 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const int k_base = (n & 15) * kKBlk + (n >> 4) * 256 + hg * 16;
   const int v_base = v_row0 * kVBlk + v_col0 * 2;
 
-  const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
 
   // One tile with the online softmax (running max, rescaled accumulators):
   // S^T = K Q^T, softmax in place on the accumulators, O^T += V^T P^T.
@@ -476,8 +497,6 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
 
   auto run = [&](auto static_tag) __attribute__((always_inline)) {
     constexpr bool kStatic = decltype(static_tag)::value;
-    issue_tile(0, 0);
-    if (n_tiles > 1) issue_tile(1, 1);
     int stage = 0;
     for (int t = 0; t < n_tiles; ++t, stage = stage == kStages - 1 ? 0 : stage + 1) {
       // This thread's part of tile t is in LDS once at most tile t+1's copies
