@@ -36,14 +36,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int u = blockIdx.x % a.Hkv;
   const int cg = blockIdx.x / a.Hkv;
-  // sequence of this chunk: chunk_off[i] <= cg < chunk_off[i + 1]
-  int lo = 0, hi = a.n_seq;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a.chunk_off[mid + 1] <= cg) lo = mid + 1; else hi = mid;
-  }
-  const int i = lo;
-  if (i >= a.n_seq) return;
+  const int i = a.chunk_seq[cg];  // chunk_off[i] <= cg < chunk_off[i + 1]
+  if (i < 0 || i >= a.n_seq) return;
   const int n_keys = a.start_pos[i] + 1;
   const int kbeg = (cg - a.chunk_off[i]) * a.chunk;
   const int kend = min(n_keys, kbeg + a.chunk);
@@ -218,8 +212,8 @@ __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
 }
 
 // chunk_off[i] = sum_{i' < i} ceil((start_pos[i'] + 1) / chunk); one workgroup.
-__global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* start_pos, int n_seq, int chunk,
-                                                      int32_t* chunk_off) {
+__global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int max_chunks,
+                                                      int32_t* chunk_off, int32_t* chunk_seq) {
   __shared__ int tmp[16];
   int carry = 0;
   for (int base = 0; base < n_seq; base += 1024) {
@@ -227,17 +221,25 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* start_pos, 
     const int v = i < n_seq ? (start_pos[i] + chunk) / chunk : 0;
     int total;
     const int ex = block_exclusive_scan(v, tmp, &total);
-    if (i < n_seq) chunk_off[i] = carry + ex;
+    if (i < n_seq) {
+      chunk_off[i] = carry + ex;
+      // the sequence of every chunk, so a split workgroup needs no search
+      // (clamped to what the host sized, so a device/host mismatch cannot
+      // write out of bounds)
+      for (int c = carry + ex; c < min(carry + ex + v, max_chunks); ++c) chunk_seq[c] = i;
+    }
     carry += total;
   }
   if (threadIdx.x == 0) chunk_off[n_seq] = carry;
+  for (int c = carry + threadIdx.x; c < max_chunks; c += 1024) chunk_seq[c] = -1;  // no sequence
 }
 
 }  // namespace
 
-hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int32_t* chunk_off,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, start_pos, n_seq, chunk, chunk_off);
+hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int max_chunks, int32_t* chunk_off,
+                              int32_t* chunk_seq, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, st, start_pos, n_seq, chunk, max_chunks, chunk_off,
+                     chunk_seq);
   return hipGetLastError();
 }
 

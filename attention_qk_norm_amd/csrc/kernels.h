@@ -83,6 +83,7 @@ struct DecodeArgs {
   int64_t cs_seq, cs_head, cs_tok;
   const int32_t* start_pos; // keys of sequence i: slots 0 .. start_pos[i] (inclusive)
   const int32_t* chunk_off; // [n_seq + 1] prefix of chunk counts
+  const int32_t* chunk_seq; // [total chunks] sequence of each chunk
   float* partial;           // [total_chunks][Hq][kPartStride]
   uint16_t* out;            // [n_seq][Hq][128]
   int n_seq, Hq, Hkv, g;
@@ -91,8 +92,8 @@ struct DecodeArgs {
 };
 constexpr int kPartStride = 132;   // 128 accumulators, m, l, 2 pad floats
 constexpr int kDecodeKeysPerPass = 128;  // 4 waves x 32 keys
-hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int32_t* chunk_off,
-                              hipStream_t st);
+hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int max_chunks, int32_t* chunk_off,
+                              int32_t* chunk_seq, hipStream_t st);
 hipError_t launch_decode_split(const DecodeArgs& a, int total_chunks, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 

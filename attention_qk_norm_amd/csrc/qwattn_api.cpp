@@ -140,7 +140,7 @@ int decode_chunk(int64_t total_keys, int n_kv_heads) {
 struct DecodeLayout {
   int chunk = 0;
   int64_t max_chunks = 0;
-  size_t off_qhat = 0, off_chunk = 0, off_part = 0, total = 0;
+  size_t off_qhat = 0, off_chunk = 0, off_chunk_seq = 0, off_part = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, int64_t total_start_pos) {
@@ -153,6 +153,8 @@ DecodeLayout decode_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
   off = align256(off + (size_t)n_seq * p->n_q_heads * QWATTN_HEAD_DIM * elem_bytes(dt));
   d.off_chunk = off;
   off = align256(off + (size_t)(n_seq + 1) * 4);
+  d.off_chunk_seq = off;
+  off = align256(off + (size_t)d.max_chunks * 4);
   d.off_part = off;
   if (dt == QWATTN_BF16) off = align256(off + (size_t)d.max_chunks * p->n_q_heads * qw::kPartStride * 4);
   d.total = off;
@@ -435,6 +437,7 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
     a.cs_seq = cache->stride_seq; a.cs_head = cache->stride_head; a.cs_tok = cache->stride_tok;
     a.start_pos = start_pos;
     a.chunk_off = (const int32_t*)(ws + dl.off_chunk);
+    a.chunk_seq = (const int32_t*)(ws + dl.off_chunk_seq);
     a.partial = (float*)(ws + dl.off_part);
     a.out = (uint16_t*)out;
     a.n_seq = n_seq;
@@ -443,7 +446,8 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
     a.g = g;
     a.chunk = dl.chunk;
     a.scale_log2e = scale_log2e(params);
-    if ((e = qw::launch_decode_plan(start_pos, n_seq, dl.chunk, (int32_t*)(ws + dl.off_chunk), strm)) != hipSuccess)
+    if ((e = qw::launch_decode_plan(start_pos, n_seq, dl.chunk, (int)dl.max_chunks, (int32_t*)(ws + dl.off_chunk),
+                                    (int32_t*)(ws + dl.off_chunk_seq), strm)) != hipSuccess)
       return hip_fail(e, "decode plan launch");
     if ((e = timed_launch(strm, [&] { return qw::launch_decode_split(a, (int)total_chunks, strm); })) != hipSuccess)
       return hip_fail(e, "decode split launch");
