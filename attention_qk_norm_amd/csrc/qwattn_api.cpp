@@ -132,7 +132,7 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
 
 // ------------------------------------------------------------------ decode plan
 int decode_chunk(int64_t total_keys, int n_kv_heads) {
-  for (int c : {1024, 512, 256})
+  for (int c : {2048, 1024, 512, 256})
     if ((total_keys / c) * n_kv_heads >= 4096) return c;
   return qw::kDecodeKeysPerPass;
 }
