@@ -58,6 +58,10 @@ def load(path=None):
     lib.qwattn_prefill.restype = i32
     lib.qwattn_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, i32, vp, vp, sz, vp]
     lib.qwattn_decode.restype = i32
+    lib.qwattn_append.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, vp, ip, i32, vp, vp, sz, vp]
+    lib.qwattn_append.restype = i32
+    lib.qwattn_append_workspace_size.argtypes = [pp, i32, i32, i64, i32]
+    lib.qwattn_append_workspace_size.restype = sz
     lib.qwattn_prefill_workspace_size.argtypes = [pp, i32, i32, i64, i32, i32]
     lib.qwattn_prefill_workspace_size.restype = sz
     lib.qwattn_decode_workspace_size.argtypes = [pp, i32, i32, i64]
@@ -187,6 +191,44 @@ def prefill(params, q, k, v, q_gamma, k_gamma, cu_seqlens, cu_seqlens_host=None,
                               cu_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc) if desc else None,
                               ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def append_workspace_size(params, dtype_code, n_seq, n_new, max_new):
+    return load().qwattn_append_workspace_size(ctypes.byref(params), dtype_code, n_seq, n_new, max_new)
+
+
+def append(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, cu_new, start_pos_host=None,
+           cu_new_host=None, out=None, workspace=None):
+    """Multi-token append against the cache: sequence s adds the tokens
+    cu_new[s] .. cu_new[s+1]-1 at positions start_pos[s] ..; their k̂/v go to
+    those cache slots and each new query attends to slots 0 .. its position."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"),
+                 (start_pos, "start_pos"), (cu_new, "cu_new")):
+        _dev(t, n)
+    sp_h = torch.as_tensor(start_pos.cpu() if start_pos_host is None else start_pos_host,
+                           dtype=torch.int32).contiguous()
+    cu_h = torch.as_tensor(cu_new.cpu() if cu_new_host is None else cu_new_host, dtype=torch.int32).contiguous()
+    n_seq = sp_h.numel()
+    if cu_h.numel() != n_seq + 1:
+        raise ValueError("cu_new must hold n_seq + 1 offsets")
+    n_new = int(cu_h[-1]) if n_seq > 0 else 0
+    max_new = int((cu_h[1:] - cu_h[:-1]).max()) if n_seq > 0 else 0
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_cache_pair(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    nbytes = append_workspace_size(params, dt, n_seq, n_new, max_new)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib.qwattn_append(ctypes.byref(params), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(q_gamma), _ptr(k_gamma),
+                             _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                             ctypes.c_void_p(start_pos.data_ptr()),
+                             sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                             ctypes.c_void_p(cu_new.data_ptr()),
+                             cu_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
     return out
 
 

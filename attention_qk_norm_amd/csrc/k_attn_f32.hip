@@ -10,7 +10,9 @@
 // FMAs plus a 4-lane reduction.  32-key K and V tiles are staged in LDS and read
 // as broadcasts.  Online softmax in fp32 (exp2 with log2(e) folded into the
 // scale).  Decode mode: one query token per sequence at start_pos, keys
-// 0 .. start_pos of the cache (the new key already appended).
+// 0 .. start_pos of the cache (the new key already appended).  Prefill mode
+// with start_pos set (an append): sequence s's rows are new tokens at
+// start_pos[s] .., attending to cache slots 0 .. their own position.
 #include "kernels.h"
 
 namespace qw {
@@ -41,11 +43,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
     L = 1;
   } else {
     row_base = a.cu[s];
-    pos0 = 0;
+    pos0 = a.start_pos ? a.start_pos[s] : 0;  // an append: new tokens at start_pos ..
     L = a.cu[s + 1] - row_base;
   }
   const int tok_base = qt * a.bm_tok;
-  if (qt < 0 || tok_base >= L) return;
+  if (qt < 0 || tok_base >= L || pos0 < 0) return;
   const int n_kv = pos0 + min(L, tok_base + a.bm_tok);
 
   const int r = tid >> 2, sub = tid & 3;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_normrope(NormRopeArgs a, int tb) {
         if ((int64_t)c <= n) lo = mid + 1; else hi = mid;
       }
       s = lo;
-      p = (int)(n - (staged ? cu_s[s] : a.cu[s]));
+      p = (int)(n - (staged ? cu_s[s] : a.cu[s])) + (a.pos ? a.pos[s] : 0);  // append: from start_pos[s]
     } else if (a.mode == kPosDecode) {
       s = (int)n;
       p = a.pos[n];

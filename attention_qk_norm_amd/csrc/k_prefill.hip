@@ -103,7 +103,12 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const int L = a.cu[s + 1] - seq0;
   const int tok_base = qt * a.bm_tok;
   if (qt < 0 || tok_base >= L) return;
-  const int n_kv = min(L, tok_base + a.bm_tok);
+  // Position of the sequence's first row: 0 for a prefill; for an append the
+  // rows are new tokens at start_pos .., the keys are cache slots 0 .. and the
+  // mask is rectangular.
+  const int p0 = a.start_pos ? a.start_pos[s] : 0;
+  if (p0 < 0) return;
+  const int n_kv = p0 + min(L, tok_base + a.bm_tok);
 
   // ---- this lane's two query rows (blocks qb = 0, 1 of the wave)
   const int n = lane & 31, hg = lane >> 5;
@@ -116,10 +121,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     const int hoff = r / a.bm_tok, toff = r - hoff * a.bm_tok;
     qtok[qb] = tok_base + toff;
     valid[qb] = hoff < a.g && qtok[qb] < L;
-    qpos[qb] = valid[qb] ? qtok[qb] : 0x3fffffff;  // padding rows see every key
+    qpos[qb] = valid[qb] ? p0 + qtok[qb] : 0x3fffffff;  // padding rows see every key
     t_head[qb] = u * a.g + hoff;
     wave_min = min(wave_min, qpos[qb]);
-    wave_max = max(wave_max, valid[qb] ? qtok[qb] : -1);
+    wave_max = max(wave_max, valid[qb] ? p0 + qtok[qb] : -1);
   }
 #pragma unroll
   for (int m = 1; m < 32; m <<= 1) {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     const double wi = a.rope.w[tid & (kHalf - 1)];  // 256 is a multiple of 64: one angle index per thread
     for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
       float c, sn;
-      rope_cos_sin(tok_base + (e >> 6), wi, c, sn);
+      rope_cos_sin(p0 + tok_base + (e >> 6), wi, c, sn);
       rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] = make_float2(c, sn);
     }
   }

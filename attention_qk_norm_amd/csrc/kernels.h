@@ -13,7 +13,7 @@ namespace qw {
 // 2 = v (copied unchanged into the cache).  heads[i] == 0 skips tensor i.
 enum NormRopeMode : int {
   kPosExplicit = 0,  // token n at position pos[n]; outputs contiguous
-  kPosPacked = 1,    // token n in sequence s (from cu), position n - cu[s]
+  kPosPacked = 1,    // token n in sequence s (from cu), position n - cu[s] (+ pos[s] if pos is set)
   kPosDecode = 2,    // token n is sequence n's new token, at position pos[n]
 };
 

@@ -233,12 +233,19 @@ size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype d
   return prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, with_cache != 0).total;
 }
 
-qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
-                             const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
-                             const int32_t* cu_seqlens_host, int32_t n_seq, void* out, void* k_cache,
-                             void* v_cache, const qwattn_cache_desc* cache, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Prefill, or (start_pos set) an append of new tokens at start_pos[s] .. against
+// the cache: the same three launches, with positions offset per sequence.
+qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                                const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t n_seq, const int32_t* start_pos,
+                                const int32_t* start_pos_host, void* out, void* k_cache, void* v_cache,
+                                const qwattn_cache_desc* cache, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const bool append = start_pos != nullptr || start_pos_host != nullptr;
   qwattn_status st;
   if ((st = check_params(params, dtype))) return st;
   const int g = params->n_q_heads / params->n_kv_heads;
@@ -262,10 +269,21 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, co
       (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")))
     return st;
   const bool any_cache = k_cache || v_cache || cache;
+  if (append) {
+    if (!start_pos || !start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos and start_pos_host are both needed");
+    if ((st = check_ptr(start_pos, "start_pos", 4))) return st;
+    if (!any_cache) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
+  }
   if (any_cache) {
     if ((st = check_cache(cache, k_cache, v_cache, dtype))) return st;
-    if (max_len > cache->capacity)
-      return fail(QWATTN_ERR_CAPACITY, "a sequence of %d tokens exceeds cache capacity %d", max_len, cache->capacity);
+    for (int s = 0; s < n_seq; ++s) {
+      const int64_t p0 = append ? start_pos_host[s] : 0;
+      const int64_t L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+      if (p0 < 0) return fail(QWATTN_ERR_INVALID_ARG, "start_pos[%d] = %lld < 0", s, (long long)p0);
+      if (p0 + L > cache->capacity)
+        return fail(QWATTN_ERR_CAPACITY, "sequence %d: %lld + %lld tokens exceed cache capacity %d", s,
+                    (long long)p0, (long long)L, cache->capacity);
+    }
   }
   if (n_tok == 0) return QWATTN_OK;
 
@@ -305,6 +323,7 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, co
     nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
   }
   nr.cu = cu_seqlens;
+  nr.pos = start_pos;  // NULL for a prefill
   nr.n_seq = n_seq;
   nr.mode = qw::kPosPacked;
   nr.n_tok = n_tok;
@@ -339,10 +358,17 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, co
     a.ks_seq = 0; a.ks_head = D; a.ks_tok = params->n_kv_heads * D;
     a.k_packed = 1;
   }
-  a.v = v;
-  a.vs_seq = 0; a.vs_head = D; a.vs_tok = params->n_kv_heads * D;
-  a.v_packed = 1;
+  if (append) {  // keys and values of the earlier tokens live only in the cache
+    a.v = v_cache;
+    a.vs_seq = cache->stride_seq; a.vs_head = cache->stride_head; a.vs_tok = cache->stride_tok;
+    a.v_packed = 0;
+  } else {
+    a.v = v;
+    a.vs_seq = 0; a.vs_head = D; a.vs_tok = params->n_kv_heads * D;
+    a.v_packed = 1;
+  }
   a.cu = cu_seqlens;
+  a.start_pos = start_pos;  // NULL for a prefill
   a.items = pa.items;
   a.out = out;
   a.n_seq = n_seq;
@@ -360,6 +386,38 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, co
   });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return QWATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                             const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t n_seq, void* out, void* k_cache,
+                             void* v_cache, const qwattn_cache_desc* cache, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return prefill_or_append(params, dtype, q, k, v, q_gamma, k_gamma, cu_seqlens, cu_seqlens_host, n_seq, nullptr,
+                           nullptr, out, k_cache, v_cache, cache, workspace, workspace_bytes, stream);
+}
+
+size_t qwattn_append_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t n_seq, int64_t n_new,
+                                    int32_t max_new) {
+  return qwattn_prefill_workspace_size(params, dtype, n_seq, n_new, max_new, 1);
+}
+
+qwattn_status qwattn_append(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                            const void* v, const void* q_gamma, const void* k_gamma, void* k_cache, void* v_cache,
+                            const qwattn_cache_desc* cache, const int32_t* start_pos, const int32_t* start_pos_host,
+                            const int32_t* cu_new, const int32_t* cu_new_host, int32_t n_seq, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (n_seq > 0 && (!start_pos || !start_pos_host))
+    return fail(QWATTN_ERR_INVALID_ARG, "start_pos and start_pos_host must be set");
+  if (n_seq > 0 && (!k_cache || !v_cache || !cache)) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
+  return prefill_or_append(params, dtype, q, k, v, q_gamma, k_gamma, cu_new, cu_new_host, n_seq, start_pos,
+                           start_pos_host, out, k_cache, v_cache, cache, workspace, workspace_bytes, stream);
 }
 
 size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t n_seq,

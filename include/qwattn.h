@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QWATTN_ABI_VERSION 1
+#define QWATTN_ABI_VERSION 2
 #define QWATTN_HEAD_DIM 128
 
 typedef enum {
@@ -136,6 +136,43 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
                             int32_t n_seq, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Multi-token append (chunked prefill) against a KV cache: the new tokens of
+ * each sequence attend to its cached keys and causally to each other, the mask
+ * being rectangular from start_pos ["第 20 章 Qwen3 与 Qwen3.5" §20.3 (new K
+ * rotated at its own positions, cached K never again) and §20.9 (appending a
+ * prompt in chunks gives the single-pass result; an over-long append is
+ * rejected and changes nothing)].
+ *   q [n_new][n_q_heads][128], k, v [n_new][n_kv_heads][128] (device): raw rows of
+ *     the new tokens of all sequences, packed one sequence after another.
+ *   cu_new [n_seq+1] (device int32) and cu_new_host (host, same values): sequence
+ *     s appends tokens cu_new[s] .. cu_new[s+1]-1; cu_new[0] = 0, non-decreasing.
+ *   start_pos [n_seq] (device int32) and start_pos_host (host, same values): the
+ *     number of tokens sequence s already holds; its new token j sits at position
+ *     start_pos[s] + j.  >= 0, and start_pos[s] + n_s <= capacity for every s,
+ *     else QWATTN_ERR_CAPACITY with nothing written.
+ *   k_cache, v_cache, cache (required): slots 0 .. start_pos[s]-1 hold K after
+ *     norm and RoPE and V; the call writes the new tokens' K (normed, rotated at
+ *     their positions) and V into slots start_pos[s] .. start_pos[s]+n_s-1, then
+ *     new token j attends to slots 0 .. start_pos[s]+j.
+ *   out [n_new][n_q_heads][128] (device).
+ *   workspace (device, >= qwattn_append_workspace_size bytes, 256-byte aligned).
+ * With every start_pos 0 this is qwattn_prefill with a cache; one new token per
+ * sequence is what qwattn_decode computes (there with a split-K kernel that
+ * suits long caches).  n_seq == 0 or n_new == 0 is a no-op. */
+qwattn_status qwattn_append(const qwattn_params* params, qwattn_dtype dtype,
+                            const void* q, const void* k, const void* v,
+                            const void* q_gamma, const void* k_gamma,
+                            void* k_cache, void* v_cache, const qwattn_cache_desc* cache,
+                            const int32_t* start_pos, const int32_t* start_pos_host,
+                            const int32_t* cu_new, const int32_t* cu_new_host,
+                            int32_t n_seq, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qwattn_append needs: n_new new tokens in all, at most max_new
+ * in one sequence (0 on invalid params). */
+size_t qwattn_append_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
+                                    int32_t n_seq, int64_t n_new, int32_t max_new);
+
 /* Workspace bytes qwattn_prefill needs for these sizes (0 on invalid params).
  * with_cache != 0 when the call will pass a cache (the rotated K goes there). */
 size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
@@ -148,10 +185,11 @@ size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dt
                                     int32_t n_seq, int64_t total_start_pos);
 
 /* Timing hook for benchmarks and profilers.  `begin` and `end` are hipEvent_t
- * handles (or both NULL to clear).  The calling thread's next qwattn_prefill or
- * qwattn_decode records `begin` on its stream right before its dominant kernel
- * (the attention kernel of prefill, the split kernel of decode) and `end` right
- * after it, then clears the hook.  Setting it enqueues nothing. */
+ * handles (or both NULL to clear).  The calling thread's next qwattn_prefill,
+ * qwattn_append or qwattn_decode records `begin` on its stream right before its
+ * dominant kernel (the attention kernel of prefill and append, the split kernel
+ * of decode) and `end` right after it, then clears the hook.  Setting it
+ * enqueues nothing. */
 qwattn_status qwattn_set_timing_events(void* begin, void* end);
 
 const char* qwattn_status_str(qwattn_status status); /* static string             */

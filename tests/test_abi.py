@@ -30,13 +30,13 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"qwattn_qk_norm_rope", "qwattn_prefill", "qwattn_decode"} <= set(names)
+    assert {"qwattn_qk_norm_rope", "qwattn_prefill", "qwattn_decode", "qwattn_append"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qwattn_abi_version() == 1
+    assert lib.qwattn_abi_version() == 2
     for st in range(6):
         assert lib.qwattn_status_str(st)
 
@@ -101,6 +101,32 @@ def test_decode_capacity_overflow_rejected(lib):
     r = lib.qwattn_decode(ctypes.byref(B.make_params(64, 2)), 1, F, F, F, F, F, F, F, ctypes.byref(d), F,
                           cu(3), 1, F, F, 1 << 30, None)
     assert r == B.ERR_UNSUPPORTED  # g = 32 > 16 on the bf16 decode path
+
+
+def append(lib, p, sp_h, cu_h, n_seq, cache, sp=F, q=F, ws_bytes=1 << 30, dtype=1):
+    kc, vc, d = cache
+    return lib.qwattn_append(ctypes.byref(p), dtype, q, F, F, F, F, kc, vc, ctypes.byref(d) if d else None, sp, sp_h,
+                             F, cu_h, n_seq, F, F, ws_bytes, None)
+
+
+def test_append_validation(lib):
+    """Appends past the capacity, negative positions, a missing cache or missing
+    positions are rejected before anything is enqueued."""
+    p = B.make_params(32, 8)
+    d = B.CacheDesc(8 * 100 * 128, 100 * 128, 128, 100)
+    c = (F, F, d)
+    assert append(lib, p, cu(90, 10), cu(0, 10, 101), 2, c) == B.ERR_CAPACITY     # 90 + 10 fits, 10 + 91 > 100
+    assert b"sequence 1" in lib.qwattn_last_error()
+    assert append(lib, p, cu(90, 0), cu(0, 11, 20), 2, c) == B.ERR_CAPACITY      # 90 + 11 > 100
+    assert b"sequence 0" in lib.qwattn_last_error()
+    assert append(lib, p, cu(-1, 0), cu(0, 1, 2), 2, c) == B.ERR_INVALID_ARG     # negative position
+    assert append(lib, p, cu(0, 0), cu(0, 1, 2), 2, (None, None, None)) == B.ERR_INVALID_ARG  # no cache
+    assert append(lib, p, None, cu(0, 1, 2), 2, c) == B.ERR_INVALID_ARG          # no host positions
+    assert append(lib, p, cu(0, 0), cu(0, 1, 2), 2, c, sp=None) == B.ERR_INVALID_ARG
+    assert append(lib, p, cu(0, 0), cu(1, 1, 2), 2, c) == B.ERR_INVALID_ARG      # cu[0] != 0
+    assert append(lib, p, cu(0, 0), cu(0, 1, 2), 2, c, ws_bytes=16) == B.ERR_WORKSPACE
+    assert append(lib, p, cu(), cu(0), 0, c) == B.OK                              # n_seq = 0: no-op
+    assert B.append_workspace_size(p, B.BF16, 2, 20, 11) == B.prefill_workspace_size(p, B.BF16, 2, 20, 11, True)
 
 
 def test_workspace_sizes(lib):

@@ -245,6 +245,131 @@ def test_prefill_full_size_sampled(case_id):
         print(case_id, s, U.bf16_gate(got, ref, spec, label=f"config {case_id} seq {s}"))
 
 
+# ------------------------------------------------------------------ append (chunked prefill)
+
+def _append_case(spec, x, splits, cap):
+    """Prefix of each sequence by prefill (cache written), then its remaining
+    tokens as one append.  splits[s] = prefix length of sequence s.  Returns the
+    append output [n_new][Hq][128], the cache and the oracle's output."""
+    dt = U.torch_dtype(spec)
+    p = U.params(spec)
+    n = spec.n_seq
+    cu = x["cu_seqlens"]
+    kc = torch.full((n, spec.n_kv_heads, cap, 128), 7.0, dtype=dt, device=U.DEV)
+    vc = torch.full_like(kc, 7.0)
+    pre = [np.arange(cu[s], cu[s] + splits[s]) for s in range(n)]
+    new = [np.arange(cu[s] + splits[s], cu[s + 1]) for s in range(n)]
+    cu_pre = np.concatenate([[0], np.cumsum([len(r) for r in pre])]).astype(np.int32)
+    cu_new = np.concatenate([[0], np.cumsum([len(r) for r in new])]).astype(np.int32)
+    ip, inew = np.concatenate(pre).astype(np.int64), np.concatenate(new).astype(np.int64)
+    g = lambda name: U.up(x[name], dt)
+    if cu_pre[-1] > 0:
+        B.prefill(p, U.up(x["q"][ip], dt), U.up(x["k"][ip], dt), U.up(x["v"][ip], dt), g("q_gamma"), g("k_gamma"),
+                  torch.from_numpy(cu_pre).to(U.DEV), cu_pre, k_cache=kc, v_cache=vc)
+    sp = np.array(splits, dtype=np.int32)
+    out = B.append(p, U.up(x["q"][inew], dt), U.up(x["k"][inew], dt), U.up(x["v"][inew], dt), g("q_gamma"),
+                   g("k_gamma"), kc, vc, torch.from_numpy(sp).to(U.DEV), torch.from_numpy(cu_new).to(U.DEV),
+                   sp, cu_new)
+    torch.cuda.synchronize()
+    ref = []
+    for s in range(n):
+        a, b, c = cu[s], cu[s] + splits[s], cu[s + 1]
+        kh = oracle.qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(splits[s]), spec.eps, spec.theta)
+        o, _ = oracle.attention_append(x["q"][b:c], x["k"][b:c], x["v"][b:c], x["q_gamma"], x["k_gamma"], kh,
+                                       x["v"][a:b], splits[s], spec.n_q_heads, spec.n_kv_heads, eps=spec.eps,
+                                       theta=spec.theta)
+        ref.append(o)
+    return out, kc, vc, np.concatenate(ref), cu_new
+
+
+APPEND_CASES = [
+    # id, dtype, Hq, Hkv, lengths (prefix + new), prefix lengths
+    (140, "bf16", 8, 2, [300, 70, 400, 5], [37, 0, 256, 4]),   # ragged prefixes, one append of a single token
+    (141, "bf16", 32, 8, [700, 129], [512, 1]),                 # g = 4 (Qwen3-8B grouping)
+    (142, "bf16", 16, 1, [333], [100]),                         # g = 16
+    (143, "f32", 8, 2, [150, 70], [64, 3]),                     # fp32 path
+]
+
+
+@pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,splits", APPEND_CASES, ids=[str(c[0]) for c in APPEND_CASES])
+def test_append_against_cache(cid, dtype, hq, hkv, lengths, splits):
+    """New tokens at start_pos .. attend to the cached keys and causally to each
+    other (rectangular mask); the oracle appends to its own cache."""
+    spec = inputs.custom_spec(cid, dtype, hq, hkv, lengths)
+    x = inputs.prefill_inputs(spec)
+    U.say(f"append case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths} prefixes={splits}")
+    out, kc, vc, ref, _ = _append_case(spec, x, splits, max(lengths) + 9)
+    got = U.down(out)
+    if dtype == "f32":
+        assert np.abs(got - ref).max() <= 1e-4, np.abs(got - ref).max()
+    else:
+        sv = np.maximum(1.0, U.v_scale_per_q_head(spec))
+        err = np.abs(got - ref) / sv[None, :, None]
+        print(f"case {cid}: scaled max {err.max():.3e} mean {err.mean():.3e}")
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    # the cache holds every token's rotated key and its value, and nothing past the sequence
+    dt = U.torch_dtype(spec)
+    cu = x["cu_seqlens"]
+    for s in range(spec.n_seq):
+        L = lengths[s]
+        pos = torch.arange(L, dtype=torch.int32, device=U.DEV)
+        _, kh = B.qk_norm_rope(U.params(spec), None, U.up(x["k"][cu[s]:cu[s + 1]], dt), None,
+                               U.up(x["k_gamma"], dt), pos)
+        torch.cuda.synchronize()
+        assert torch.equal(kc[s, :, :L], kh.permute(1, 0, 2))
+        assert torch.equal(vc[s, :, :L], U.up(x["v"][cu[s]:cu[s + 1]], dt).permute(1, 0, 2))
+        assert bool((kc[s, :, L:] == 7.0).all()) and bool((vc[s, :, L:] == 7.0).all())
+
+
+def test_append_in_chunks_equals_one_prefill():
+    """Appending a prompt in chunks [0:2], [2:5], [5:6] and then in larger
+    ragged chunks gives the single-pass prefill rows, as the pages' own
+    KV-cache check has it.  Here bit for bit: a row's keys are visited in the
+    same 64-key tiles from slot 0 either way, and masked keys add exact zeros."""
+    spec = inputs.custom_spec(144, "bf16", 8, 2, [300])
+    x = inputs.prefill_inputs(spec)
+    dt = torch.bfloat16
+    p = U.params(spec)
+    full = U.down(U.run_prefill(spec, x))
+    U.say("append in chunks vs one prefill")
+    kc = torch.zeros(1, 2, 320, 128, dtype=dt, device=U.DEV)
+    vc = torch.zeros_like(kc)
+    g = lambda name: U.up(x[name], dt)
+    outs = []
+    for a, b in ((0, 2), (2, 5), (5, 6), (6, 70), (70, 71), (71, 300)):
+        sp = np.array([a], dtype=np.int32)
+        cn = np.array([0, b - a], dtype=np.int32)
+        o = B.append(p, U.up(x["q"][a:b], dt), U.up(x["k"][a:b], dt), U.up(x["v"][a:b], dt), g("q_gamma"),
+                     g("k_gamma"), kc, vc, torch.from_numpy(sp).to(U.DEV), torch.from_numpy(cn).to(U.DEV), sp, cn)
+        outs.append(U.down(o))
+    torch.cuda.synchronize()
+    got = np.concatenate(outs)
+    sv = np.maximum(1.0, U.v_scale_per_q_head(spec))
+    err = np.abs(got - full) / sv[None, :, None]
+    print(f"chunks vs one pass: scaled max {err.max():.3e}; bitwise equal rows {np.mean(np.all(got == full, axis=(1, 2))):.2f}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    assert np.array_equal(got, full)
+
+
+def test_append_capacity_rejection_leaves_cache():
+    """An append that would run past the cache is rejected and changes nothing."""
+    spec = inputs.custom_spec(145, "bf16", 8, 2, [40])
+    x = inputs.prefill_inputs(spec)
+    dt = torch.bfloat16
+    kc = torch.full((1, 2, 40, 128), 3.0, dtype=dt, device=U.DEV)
+    vc = torch.full_like(kc, 3.0)
+    before = (kc.clone(), vc.clone())
+    sp = np.array([30], dtype=np.int32)
+    cn = np.array([0, 11], dtype=np.int32)
+    U.say("append past capacity")
+    with pytest.raises(B.QwattnError):
+        B.append(U.params(spec), U.up(x["q"][:11], dt), U.up(x["k"][:11], dt), U.up(x["v"][:11], dt),
+                 U.up(x["q_gamma"], dt), U.up(x["k_gamma"], dt), kc, vc, torch.from_numpy(sp).to(U.DEV),
+                 torch.from_numpy(cn).to(U.DEV), sp, cn)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, before[0]) and torch.equal(vc, before[1])
+
+
 # ------------------------------------------------------------------ decode
 
 DECODE_SMALL = [
