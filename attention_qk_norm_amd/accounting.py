@@ -32,3 +32,14 @@ def decode_total_bytes(cached_lengths, n_q_heads, n_kv_heads, head_dim=128, elem
     n = len(cached_lengths)
     per_seq = elem_bytes * head_dim * (n_q_heads + 2 * n_kv_heads + 2 * n_kv_heads + n_q_heads)
     return decode_kv_read_bytes(cached_lengths, n_kv_heads, head_dim, elem_bytes) + n * per_seq
+
+
+def append_pairs(start_positions, new_lengths):
+    """Unmasked (query, key) pairs per query head of an append: new token j of a
+    sequence with p cached tokens sees p + j + 1 keys, so n p + n (n + 1) / 2."""
+    return sum(int(n) * int(p) + int(n) * (int(n) + 1) // 2 for p, n in zip(start_positions, new_lengths))
+
+
+def append_flops(start_positions, new_lengths, n_q_heads, head_dim=128):
+    """4 d flops per unmasked pair and query head, as for prefill."""
+    return 4 * head_dim * n_q_heads * append_pairs(start_positions, new_lengths)

@@ -143,6 +143,61 @@ def run_decode(st):
              out=st["out"], workspace=st["ws"])
 
 
+def measure_append(dev, n_calls=10, new_tokens=512):
+    """Chunked prefill against the cache (qwattn_append), on the 4 x 4096
+    workload: each sequence's first 4096 - new_tokens tokens are prefilled into
+    the cache, then its last new_tokens tokens are appended (timed; every call
+    rewrites the same cache slots)."""
+    import torch
+    from attention_qk_norm_amd import accounting, binding as B, inputs
+    spec = inputs.case_spec(1)
+    x = inputs.prefill_inputs(spec)
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+    cu = x["cu_seqlens"]
+    split = [L - new_tokens for L in spec.lengths]
+    pre = np.concatenate([np.arange(cu[s], cu[s] + split[s]) for s in range(spec.n_seq)])
+    new = np.concatenate([np.arange(cu[s] + split[s], cu[s + 1]) for s in range(spec.n_seq)])
+    cu_pre = np.concatenate([[0], np.cumsum(split)]).astype(np.int32)
+    cu_new = np.arange(spec.n_seq + 1, dtype=np.int32) * new_tokens
+    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    cap = (max(spec.lengths) + 63) // 64 * 64
+    kc = torch.empty(spec.n_seq, spec.n_kv_heads, cap, 128, dtype=bf, device=dev)
+    vc = torch.empty_like(kc)
+    qg, kg = up(x["q_gamma"]), up(x["k_gamma"])
+    B.prefill(p, up(x["q"][pre]), up(x["k"][pre]), up(x["v"][pre]), qg, kg, torch.from_numpy(cu_pre).to(dev),
+              cu_pre, k_cache=kc, v_cache=vc)
+    q, k, v = up(x["q"][new]), up(x["k"][new]), up(x["v"][new])
+    sp_h = np.array(split, dtype=np.int32)
+    sp, cn = torch.from_numpy(sp_h).to(dev), torch.from_numpy(cu_new).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(B.append_workspace_size(p, B.BF16, spec.n_seq, int(cu_new[-1]), new_tokens),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: B.append(p, q, k, v, qg, kg, kc, vc, sp, cn, sp_h, cu_new, out=out, workspace=ws)
+    for _ in range(2):
+        run()
+    ev = HipEvents()
+    kev = [(ev.create(), ev.create()) for _ in range(n_calls)]
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for (ka, kb), (ca, cb) in zip(kev, cev):
+        B.set_timing_events(ka, kb)
+        ca.record()
+        run()
+        cb.record()
+    torch.cuda.synchronize()
+    flops = accounting.append_flops(split, [new_tokens] * spec.n_seq, spec.n_q_heads)
+    k_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in kev]))
+    c_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+    return {"metric": "append attention TFLOP/s", "unit": "TFLOP/s",
+            "workload": f"qwen3-8b-append-bf16 {spec.n_seq}x({split[0]} cached + {new_tokens} new) Hq{spec.n_q_heads} Hkv{spec.n_kv_heads}",
+            "value": round(flops / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
+            "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(flops / (k_ms * 1e-3) / 1e12, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
+
+
 def cpu_baseline_prefill(spec, n_sample=3):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     the first `n_sample` whole sequences of the packed batch (all query heads,
@@ -182,6 +237,7 @@ def main():
     ap.add_argument("--decode-case", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the chunked-prefill (append) measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -267,6 +323,9 @@ def main():
                          "traffic": recorded_traffic("k_decode_split", "k_decode.hip") if args.decode_case == 2 else None,
                          "kernel_ms": round(split_ms, 4)},
         }
+    if not args.no_append:
+        log("append (chunked prefill) measurement")
+        rec["append"] = measure_append(dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
