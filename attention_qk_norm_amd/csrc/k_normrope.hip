@@ -4,7 +4,8 @@
 // the mean taken in fp32, then scaled by gamma ("7.2 Qwen3 全规模实现" §7.2.1
 // RMSNorm; "Qwen3" notes, "QK-Norm").  RoPE: dims i and i+64 of a row at
 // position p turn by p * theta^(-2i/128) ("7.2 Qwen3 全规模实现" §7.2.1 RoPE).
-// The norm comes first, as four of the five pages print it.
+// The norm comes first, as four of the five pages print it; order = 1 gives the
+// other order ("Transformer 20. Qwen 3 架构拆解" §2.2: RoPE, then the norm).
 //
 // A workgroup owns `tb` consecutive tokens (16 for large inputs, down to one
 // for a decode step).  It first finds each token's sequence and position, then
@@ -176,12 +177,20 @@ __global__ __launch_bounds__(256) void k_normrope(NormRopeArgs a, int tb) {
         for (int e = 0; e < 8; ++e) ss += xo[e] * xo[e];
         ss = row16_sum(ss);
         const float inv = rsqrtf(ss * (1.0f / kD) + a.eps);
+        // RMS is rotation-invariant, so one inv serves both orders; they differ
+        // in whether gamma scales the dims before the rotation (norm first) or
+        // after it (RoPE first).
         float y[8];
+        if (a.order == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float own = xo[e] * inv * go[e];
-          const float par = xp[e] * inv * gp[e];
-          y[e] = own * cs[e] + sgn * (par * sn[e]);
+          for (int e = 0; e < 8; ++e) {
+            const float own = xo[e] * inv * go[e];
+            const float par = xp[e] * inv * gp[e];
+            y[e] = own * cs[e] + sgn * (par * sn[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (xo[e] * cs[e] + sgn * (xp[e] * sn[e])) * inv * go[e];
         }
         T* dst;
         if (which == 1 && a.k_cache)

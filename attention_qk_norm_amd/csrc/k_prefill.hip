@@ -256,14 +256,20 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
       for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
     ss = pair_sum(ss);  // lane l ^ 32 holds the other half of the row
     const float inv = rsqrtf(ss * (1.0f / kD) + a.eps);
+    // RMS is rotation-invariant, so one inv serves both orders; they differ in
+    // whether gamma scales the dims before the rotation (norm first, order 0)
+    // or after it (RoPE first, order 1).
+    auto scale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+      for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[kk][2 * e] *= inv * bf16_lo(graw[kk][e]);
-        x[kk][2 * e + 1] *= inv * bf16_hi(graw[kk][e]);
+        for (int e = 0; e < 4; ++e) {
+          x[kk][2 * e] *= inv * bf16_lo(graw[kk][e]);
+          x[kk][2 * e + 1] *= inv * bf16_hi(graw[kk][e]);
+        }
       }
-    }
+    };
+    if (a.order == 0) scale();
     const float2* cs = rope_t + (ok ? tok - tok_base : 0) * kRopeRow + 8 * hg;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -275,6 +281,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
         x[kk + 4][e] = y2 * v.x + y1 * v.y;
       }
     }
+    if (a.order != 0) scale();
     // The fragments are only ever MFMA B operands, which gfx950 reads from
     // AGPRs directly: writing them there keeps the 64 registers out of the
     // VGPR file that the tile loop fills with scores, weights and O.

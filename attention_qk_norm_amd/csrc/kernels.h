@@ -31,6 +31,7 @@ struct NormRopeArgs {
   int mode;
   int64_t n_tok;
   float eps;
+  int order;                // 0: QK-Norm then RoPE; 1: RoPE then QK-Norm
   RopeFreq rope;
 };
 
@@ -61,13 +62,15 @@ struct PrefillArgs {
   int64_t vs_seq, vs_head, vs_tok;
   int v_packed;
   const int32_t* cu;        // packed: sequence offsets; decode: unused
-  const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token
+  const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token;
+                            // prefill: NULL, or (an append) position of each sequence's first row
   const int2* items;
   void* out;
   int n_seq, Hq, Hkv, g, bm_tok;
   int decode;               // fp32 path: items are (seq, 0), one query token at start_pos
   float scale_log2e;        // softmax scale * log2(e)
   float eps;
+  int order;                // bf16 Q prologue: 0 QK-Norm then RoPE, 1 RoPE then QK-Norm
   RopeFreq rope;
 };
 constexpr int kPrefillRows = 256;  // query rows (g heads x bm_tok tokens) per workgroup

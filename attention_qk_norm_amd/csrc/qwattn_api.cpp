@@ -66,8 +66,7 @@ qwattn_status check_params(const qwattn_params* p, qwattn_dtype dt) {
     return fail(QWATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
   if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale))
     return fail(QWATTN_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (p->order == 1) return fail(QWATTN_ERR_UNSUPPORTED, "order=1 (RoPE then norm) is not implemented");
-  if (p->order != 0) return fail(QWATTN_ERR_INVALID_ARG, "order must be 0");
+  if (p->order != 0 && p->order != 1) return fail(QWATTN_ERR_INVALID_ARG, "order must be 0 or 1");
   return QWATTN_OK;
 }
 
@@ -216,6 +215,7 @@ qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtyp
   a.mode = qw::kPosExplicit;
   a.n_tok = n_tok;
   a.eps = params->eps;
+  a.order = params->order;
   a.rope = rope_freq(params->rope_theta);
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
@@ -328,6 +328,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   nr.mode = qw::kPosPacked;
   nr.n_tok = n_tok;
   nr.eps = params->eps;
+  nr.order = params->order;
   nr.rope = rope;
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
   if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
@@ -379,6 +380,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.decode = 0;
   a.scale_log2e = scale_log2e(params);
   a.eps = params->eps;
+  a.order = params->order;
   a.rope = rope;
   e = timed_launch(strm, [&] {
     return dtype == QWATTN_BF16 ? qw::launch_prefill_bf16(a, (int)n_items, strm)
@@ -483,6 +485,7 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
   nr.mode = qw::kPosDecode;
   nr.n_tok = n_seq;
   nr.eps = params->eps;
+  nr.order = params->order;
   nr.rope = rope_freq(params->rope_theta);
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
   if (e != hipSuccess) return hip_fail(e, "decode prologue launch");

@@ -10,8 +10,11 @@
  *   RoPE      rotate-half: dims i and i + head_dim/2 of a head vector at position p
  *             turn by the angle p * theta^(-2i/head_dim).
  *             ["7.2 Qwen3 全规模实现" §7.2.1 RoPE]
- *   order     QK-Norm first, then RoPE (the order four of the five pages print;
- *             "Transformer 20. Qwen 3 架构拆解" §2.2 claims the reverse).
+ *   order     QK-Norm first, then RoPE (the order four of the five pages print);
+ *             params.order = 1 selects RoPE first, then QK-Norm, the order
+ *             "Transformer 20. Qwen 3 架构拆解" §2.2 describes.  The RMS is the same
+ *             either way (RoPE keeps norms); the orders differ in whether gamma
+ *             scales the dims before or after the rotation.
  *   attention causal softmax(Q K^T / sqrt(head_dim)) V per query head t, reading
  *             KV head floor(t / g), g = n_q_heads / n_kv_heads.
  *             ["Transformer 20. Qwen 3 架构拆解" §2.2; "7.2 Qwen3 全规模实现" §7.2.1 GQA]
@@ -68,7 +71,7 @@ typedef struct {
   float eps;            /* RMSNorm epsilon (1e-6 for Qwen3), >= 0                  */
   double rope_theta;    /* RoPE base (1e6 dense Qwen3, 1e7 for the MoE models), > 1 */
   float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                   */
-  int32_t order;        /* 0 = QK-Norm then RoPE (the only value accepted)         */
+  int32_t order;        /* 0 = QK-Norm then RoPE, 1 = RoPE then QK-Norm            */
 } qwattn_params;
 
 /* A KV cache: element (seq s, kv head h, slot j, dim d) of k_cache / v_cache is at

@@ -18,7 +18,7 @@ Page references used below:
 
 Readings where the pages are silent or disagree (each is listed in the design doc):
   * order: norm then RoPE ([RL], [NW], [XW], [OZ]); [QA] claims RoPE then norm.
-    Both are available through ``order``; the product path implements the first.
+    Both are available through ``order`` (the library too, as params.order).
   * eps sits inside the square root, added to the mean square ([XW] RMSNorm;
     the [QA] §2.3 formula is garbled).
   * one gamma of length head_dim for Q and one for K, shared by all heads.

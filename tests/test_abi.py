@@ -59,7 +59,6 @@ def prefill(lib, p, cu_h, n_seq, q=F, cache=(None, None, None), ws=F, ws_bytes=1
     (dict(n_q_heads=30, n_kv_heads=8), B.ERR_INVALID_ARG),
     (dict(n_q_heads=0, n_kv_heads=8), B.ERR_INVALID_ARG),
     (dict(n_q_heads=32, n_kv_heads=8, head_dim=64), B.ERR_UNSUPPORTED),
-    (dict(n_q_heads=32, n_kv_heads=8, order=1), B.ERR_UNSUPPORTED),
     (dict(n_q_heads=32, n_kv_heads=8, order=2), B.ERR_INVALID_ARG),
     (dict(n_q_heads=32, n_kv_heads=8, rope_theta=1.0), B.ERR_INVALID_ARG),
     (dict(n_q_heads=32, n_kv_heads=8, eps=-1.0), B.ERR_INVALID_ARG),

@@ -370,6 +370,84 @@ def test_append_capacity_rejection_leaves_cache():
     assert torch.equal(kc, before[0]) and torch.equal(vc, before[1])
 
 
+# ------------------------------------------------------------------ RoPE-then-norm order (params.order = 1)
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_norm_order_all_entry_points(dtype):
+    """params.order = 1 (RoPE first, then QK-Norm) on every entry point against
+    the oracle's order="rope_norm"; with the configs' non-pair-symmetric gamma
+    the two orders give different outputs, and the library follows each."""
+    spec = inputs.custom_spec(146 if dtype == "bf16" else 147, dtype, 8, 2, [1, 70, 200])
+    x = inputs.prefill_inputs(spec)
+    dt = U.torch_dtype(spec)
+    p1 = U.params(spec, order=1)
+    cu = x["cu_seqlens"]
+    U.say(f"RoPE-then-norm order, {dtype}")
+    kw = dict(eps=spec.eps, theta=spec.theta)
+
+    def check(got, ref, label):
+        if dtype == "f32":
+            assert np.abs(got - ref).max() <= 1e-4, (label, np.abs(got - ref).max())
+        else:
+            sv = np.maximum(1.0, U.v_scale_per_q_head(spec))
+            err = np.abs(got - ref) / sv[None, :, None]
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3, (label, err.max(), err.mean())
+
+    # standalone rows
+    pos = np.arange(cu[-1], dtype=np.int32) % 97
+    qo, ko = B.qk_norm_rope(p1, U.up(x["q"], dt), U.up(x["k"], dt), U.up(x["q_gamma"], dt), U.up(x["k_gamma"], dt),
+                            torch.from_numpy(pos).to(U.DEV))
+    torch.cuda.synchronize()
+    for got, raw, g in ((qo, x["q"], x["q_gamma"]), (ko, x["k"], x["k_gamma"])):
+        ref = oracle.qk_norm_rope(raw, g, pos, spec.eps, spec.theta, order="rope_norm")
+        tol = 2e-5 if dtype == "f32" else None
+        got = U.down(got)
+        if tol:
+            assert np.abs(got - ref).max() <= tol
+        else:
+            assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5)
+    # prefill (with a cache, which then serves the append and decode below)
+    cap = 210
+    kc = torch.zeros(3, 2, cap, 128, dtype=dt, device=U.DEV)
+    vc = torch.zeros_like(kc)
+    out = B.prefill(p1, U.up(x["q"], dt), U.up(x["k"], dt), U.up(x["v"], dt), U.up(x["q_gamma"], dt),
+                    U.up(x["k_gamma"], dt), torch.from_numpy(cu).to(U.DEV), cu, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    ref1 = oracle.attention_prefill(x["q"], x["k"], x["v"], x["q_gamma"], x["k_gamma"], cu, 8, 2,
+                                    order="rope_norm", **kw)
+    ref0 = oracle.attention_prefill(x["q"], x["k"], x["v"], x["q_gamma"], x["k_gamma"], cu, 8, 2, **kw)
+    check(U.down(out), ref1, "prefill")
+    assert np.abs(ref1 - ref0).max() > 0.1  # the orders really differ here
+    # one more token per sequence, once through append and once through decode
+    rng = np.random.default_rng(7)
+    qn = inputs.round_to_bf16(rng.standard_normal((3, 8, 128))) if dtype == "bf16" else \
+        rng.standard_normal((3, 8, 128)).astype(np.float32)
+    kn = inputs.round_to_bf16(rng.standard_normal((3, 2, 128))) if dtype == "bf16" else \
+        rng.standard_normal((3, 2, 128)).astype(np.float32)
+    vn = inputs.round_to_bf16(rng.standard_normal((3, 2, 128))) if dtype == "bf16" else \
+        rng.standard_normal((3, 2, 128)).astype(np.float32)
+    sp = np.array(spec.lengths, dtype=np.int32)
+    refs = []
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        kh = oracle.qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(b - a), spec.eps, spec.theta,
+                                 order="rope_norm")
+        o, _ = oracle.attention_append(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], x["q_gamma"], x["k_gamma"], kh,
+                                       x["v"][a:b], sp[i], 8, 2, order="rope_norm", **kw)
+        refs.append(o[0])
+    ref = np.stack(refs)
+    cn = np.arange(4, dtype=np.int32)
+    kc2, vc2 = kc.clone(), vc.clone()
+    o_app = B.append(p1, U.up(qn, dt), U.up(kn, dt), U.up(vn, dt), U.up(x["q_gamma"], dt), U.up(x["k_gamma"], dt),
+                     kc2, vc2, torch.from_numpy(sp).to(U.DEV), torch.from_numpy(cn).to(U.DEV), sp, cn)
+    o_dec = B.decode(p1, U.up(qn, dt), U.up(kn, dt), U.up(vn, dt), U.up(x["q_gamma"], dt), U.up(x["k_gamma"], dt),
+                     kc, vc, torch.from_numpy(sp).to(U.DEV), sp)
+    torch.cuda.synchronize()
+    check(U.down(o_app), ref, "append")
+    check(U.down(o_dec), ref, "decode")
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)  # both wrote the same new key and value
+
+
 # ------------------------------------------------------------------ decode
 
 DECODE_SMALL = [
