@@ -223,12 +223,16 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
     issue_tile(0, 0);
     if (n_tiles > 1) issue_tile(1, 1);
   }
+  // The angle is reduced in fp64 (whole turns removed exactly) and evaluated
+  // by the hardware sine/cosine, which take turns: errors near 1e-6, far below
+  // the bf16 rounding of the fragments they feed.
   {
-    const double wi = a.rope.w[tid & (kHalf - 1)];  // 256 is a multiple of 64: one angle index per thread
+    const double turns = a.rope.w[tid & (kHalf - 1)] * 0.15915494309189535;  // w / (2 pi); one angle per thread
     for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
-      float c, sn;
-      rope_cos_sin(p0 + tok_base + (e >> 6), wi, c, sn);
-      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] = make_float2(c, sn);
+      const double x = (double)(p0 + tok_base + (e >> 6)) * turns;
+      const float r = (float)(x - rint(x));  // in [-1/2, 1/2] turn
+      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] =
+          make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
     }
   }
   __syncthreads();
