@@ -31,9 +31,9 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
     s = blockIdx.x / a.Hkv;
     qt = 0;
   } else {
-    const int2 item = a.items[blockIdx.x / a.Hkv];
-    s = item.x;
-    qt = item.y;
+    const PrefillItem item = a.items[blockIdx.x / a.Hkv];
+    s = item.s;
+    qt = item.qt;
   }
   if (s < 0 || s >= a.n_seq) return;
   int row_base, L, pos0;

@@ -96,17 +96,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int u = blockIdx.x % a.Hkv;
-  const int2 item = a.items[blockIdx.x / a.Hkv];
-  const int s = item.x, qt = item.y;
+  const PrefillItem item = a.items[blockIdx.x / a.Hkv];
+  const int s = item.s, qt = item.qt;
   if (s < 0 || s >= a.n_seq) return;
-  const int seq0 = a.cu[s];
-  const int L = a.cu[s + 1] - seq0;
+  const int seq0 = item.seq0;
+  const int L = item.len;
   const int tok_base = qt * a.bm_tok;
   if (qt < 0 || tok_base >= L) return;
   // Position of the sequence's first row: 0 for a prefill; for an append the
   // rows are new tokens at start_pos .., the keys are cache slots 0 .. and the
   // mask is rectangular.
-  const int p0 = a.start_pos ? a.start_pos[s] : 0;
+  const int p0 = item.p0;
   if (p0 < 0) return;
   const int n_kv = p0 + min(L, tok_base + a.bm_tok);
 
@@ -616,7 +616,13 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
     const int rk = rank[s];
     for (int q = tid; q < nt; q += 1024) {
       const int pos = off[q] + rk;
-      if (pos < a.n_items) a.items[pos] = make_int2(s, q);
+      if (pos < a.n_items) {
+        PrefillItem it;
+        it.s = s; it.qt = q; it.seq0 = a.cu[s]; it.len = a.cu[s + 1] - a.cu[s];
+        it.p0 = a.start_pos ? a.start_pos[s] : 0;
+        it.pad0 = it.pad1 = it.pad2 = 0;
+        a.items[pos] = it;
+      }
     }
   }
 }

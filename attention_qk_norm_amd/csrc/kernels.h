@@ -38,6 +38,12 @@ struct NormRopeArgs {
 hipError_t launch_normrope(bool bf16, const NormRopeArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill
+// One entry of the work list: query tile qt of sequence s, with what a
+// workgroup needs next (its rows' token offset and count, and the position of
+// the sequence's first row), so that it starts with a single dependent load.
+struct PrefillItem {
+  int32_t s, qt, seq0, len, p0, pad0, pad1, pad2;
+};
 // Work list of (sequence, query tile) pairs, heaviest first.
 struct PlanArgs {
   const int32_t* cu;
@@ -46,7 +52,8 @@ struct PlanArgs {
   int max_tiles;     // max over sequences of ceil(L / bm_tok)
   int n_items;       // sum over sequences of ceil(L / bm_tok)
   int32_t* scratch;  // 4 * (max_tiles + 1) + n_seq ints
-  int2* items;
+  const int32_t* start_pos;  // NULL, or (an append) the position of each sequence's first row
+  PrefillItem* items;
 };
 hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
 
@@ -64,7 +71,7 @@ struct PrefillArgs {
   const int32_t* cu;        // packed: sequence offsets; decode: unused
   const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token;
                             // prefill: NULL, or (an append) position of each sequence's first row
-  const int2* items;
+  const PrefillItem* items;
   void* out;
   int n_seq, Hq, Hkv, g, bm_tok;
   int decode;               // fp32 path: items are (seq, 0), one query token at start_pos

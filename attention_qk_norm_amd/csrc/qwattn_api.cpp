@@ -124,7 +124,7 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
   pl.off_scratch = off;
   off = align256(off + (size_t)(4 * ((int64_t)max_tiles + 1) + n_seq) * 4);
   pl.off_items = off;
-  off = align256(off + (size_t)n_items * 8);
+  off = align256(off + (size_t)n_items * sizeof(qw::PrefillItem));
   pl.total = off;
   return pl;
 }
@@ -341,7 +341,8 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   pa.max_tiles = max_tiles;
   pa.n_items = (int)n_items;
   pa.scratch = (int32_t*)(ws + pl.off_scratch);
-  pa.items = (int2*)(ws + pl.off_items);
+  pa.start_pos = start_pos;  // NULL for a prefill
+  pa.items = (qw::PrefillItem*)(ws + pl.off_items);
   if ((e = qw::launch_prefill_plan(pa, strm)) != hipSuccess) return hip_fail(e, "plan launch");
 
   // 3) attention
