@@ -177,24 +177,10 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   // Lane (n, hg) holds dims 16kk + 8hg + e (kk < 8, e < 8); dims i and i + 64 of
   // a rotation pair sit in fragments kk and kk + 4 of the same lane.
   bf16x8 qf[2][8];
-  // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
-  // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
-  // norms), so |logit| * log2(e) <= c * 128 * max|gamma_q| * max|gamma_k| with
-  // c = scale * log2(e), plus a margin for the bf16 roundings.
-  float kmax, qmax;
-  {
-    const uint16_t* gk = (const uint16_t*)a.k_gamma;
-    const uint16_t* gq = (const uint16_t*)a.q_gamma;
-    kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * lane])), fabsf(bf16_to_f32(gk[2 * lane + 1])));
-    qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * lane])), fabsf(bf16_to_f32(gq[2 * lane + 1])));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
-      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
-    }
-  }
+  // The launch-wide logit bound (decided once by the plan kernel) picks the
+  // softmax form.
+  const bool use_static = a.static_flag[0] != 0;
   const float c_log2 = a.scale_log2e;
-  const bool use_static = c_log2 * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
   // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
   // scores come out in log2 units), into bf16 fragments.  Called once per query
   // block with static arguments, so the fragment arrays stay in registers.
@@ -585,6 +571,24 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
     const int L = max(0, a.cu[s + 1] - a.cu[s]);
     return min(a.max_tiles, (L + a.bm_tok - 1) / a.bm_tok);
   };
+  if (tid < 64 && a.static_flag) {
+    // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
+    // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
+    // norms), so with the query rows pre-scaled by c = scale * log2(e),
+    // |score| <= c * 128 * max|gamma_q| * max|gamma_k|, plus a margin for the
+    // bf16 roundings.  Within 60 (log2 units) every p = 2^score is a normal
+    // float, and the prefill runs its static-bound softmax.
+    const uint16_t* gk = (const uint16_t*)a.k_gamma;
+    const uint16_t* gq = (const uint16_t*)a.q_gamma;
+    float kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * tid])), fabsf(bf16_to_f32(gk[2 * tid + 1])));
+    float qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * tid])), fabsf(bf16_to_f32(gq[2 * tid + 1])));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
+      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
+    }
+    if (tid == 0) a.static_flag[0] = a.scale_log2e * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+  }
   for (int i = tid; i < nb; i += 1024) { hist[i] = 0; tie[i] = 0; }
   __syncthreads();
   for (int s = tid; s < a.n_seq; s += 1024) atomicAdd(&hist[n_tiles_of(s)], 1);

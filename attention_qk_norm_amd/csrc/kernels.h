@@ -54,6 +54,11 @@ struct PlanArgs {
   int32_t* scratch;  // 4 * (max_tiles + 1) + n_seq ints
   const int32_t* start_pos;  // NULL, or (an append) the position of each sequence's first row
   PrefillItem* items;
+  // bf16 path: the QK-Norm logit bound of the launch decides the softmax form
+  const void* q_gamma;       // NULL on the fp32 path
+  const void* k_gamma;
+  float scale_log2e;
+  int32_t* static_flag;      // out: 1 when the static-bound softmax applies
 };
 hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
 
@@ -72,6 +77,7 @@ struct PrefillArgs {
   const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token;
                             // prefill: NULL, or (an append) position of each sequence's first row
   const PrefillItem* items;
+  const int32_t* static_flag;  // bf16 path: written by the plan kernel
   void* out;
   int n_seq, Hq, Hkv, g, bm_tok;
   int decode;               // fp32 path: items are (seq, 0), one query token at start_pos

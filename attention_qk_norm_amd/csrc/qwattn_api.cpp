@@ -104,7 +104,7 @@ float scale_log2e(const qwattn_params* p) {
 // ------------------------------------------------------------------ prefill plan
 struct PrefillPlan {
   int g = 1, bm_tok = 1, max_tiles = 0, n_items = 0;
-  size_t off_khat = 0, off_qhat = 0, off_scratch = 0, off_items = 0, total = 0;
+  size_t off_khat = 0, off_qhat = 0, off_scratch = 0, off_items = 0, off_flag = 0, total = 0;
 };
 
 // Workspace layout; n_items / max_tiles are upper bounds when `exact` is false.
@@ -125,6 +125,8 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
   off = align256(off + (size_t)(4 * ((int64_t)max_tiles + 1) + n_seq) * 4);
   pl.off_items = off;
   off = align256(off + (size_t)n_items * sizeof(qw::PrefillItem));
+  pl.off_flag = off;
+  off = align256(off + 4);
   pl.total = off;
   return pl;
 }
@@ -343,6 +345,12 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   pa.scratch = (int32_t*)(ws + pl.off_scratch);
   pa.start_pos = start_pos;  // NULL for a prefill
   pa.items = (qw::PrefillItem*)(ws + pl.off_items);
+  if (dtype == QWATTN_BF16) {
+    pa.q_gamma = q_gamma;
+    pa.k_gamma = k_gamma;
+    pa.scale_log2e = scale_log2e(params);
+    pa.static_flag = (int32_t*)(ws + pl.off_flag);
+  }
   if ((e = qw::launch_prefill_plan(pa, strm)) != hipSuccess) return hip_fail(e, "plan launch");
 
   // 3) attention
@@ -372,6 +380,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.cu = cu_seqlens;
   a.start_pos = start_pos;  // NULL for a prefill
   a.items = pa.items;
+  a.static_flag = pa.static_flag;
   a.out = out;
   a.n_seq = n_seq;
   a.Hq = params->n_q_heads;
