@@ -95,19 +95,20 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  // Consecutive workgroups take the KV heads of one work item, so each XCD
+  // (workgroups are dealt round-robin over the 8 XCDs) keeps to its own heads
+  // and their K/V stay in its L2.
   const int u = blockIdx.x % a.Hkv;
   const PrefillItem item = a.items[blockIdx.x / a.Hkv];
   const int s = item.s, qt = item.qt;
-  if (s < 0 || s >= a.n_seq) return;
   const int seq0 = item.seq0;
   const int L = item.len;
   const int tok_base = qt * a.bm_tok;
-  if (qt < 0 || tok_base >= L) return;
   // Position of the sequence's first row: 0 for a prefill; for an append the
   // rows are new tokens at start_pos .., the keys are cache slots 0 .. and the
   // mask is rectangular.
   const int p0 = item.p0;
-  if (p0 < 0) return;
+  if ((s < 0) | (s >= a.n_seq) | (qt < 0) | (tok_base >= L) | (p0 < 0)) return;
   const int n_kv = p0 + min(L, tok_base + a.bm_tok);
 
   // ---- this lane's two query rows (blocks qb = 0, 1 of the wave)
