@@ -64,6 +64,8 @@ constexpr int kStageBytes = kKTile + kVTile;
 // Three-stage ring: tile t is read while tiles t+1 and t+2 are in flight.
 constexpr int kStages = 3;
 constexpr int kLoadsPerTile = 8;  // direct loads per lane per tile (4 K blocks, 4 V blocks)
+constexpr int kPlanLdsTiles = 2047;  // plans up to this many tiles per sequence ...
+constexpr int kPlanLdsSeqs = 2047;   // ... and sequences run entirely in LDS
 constexpr int kRopeRow = kHalf + 2;  // float2 entries per row of the cos/sin table (16 B pad)
 // Dynamic LDS: the K/V ring, or the prologue's cos/sin table if that is larger
 // (bm_tok = 256 / g tokens; at most 256).
@@ -561,37 +563,27 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
 // write out of bounds.
 __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
   __shared__ int tmp[16];
+  // Small plans (the usual case) keep every array in LDS; larger ones use the
+  // caller's scratch.
+  __shared__ int32_t lds_arr[4 * (kPlanLdsTiles + 1) + 2 * (kPlanLdsSeqs + 1)];
   const int tid = threadIdx.x;
   const int nb = a.max_tiles + 1;
-  int32_t* hist = a.scratch;
+  const bool small = a.max_tiles <= kPlanLdsTiles && a.n_seq <= kPlanLdsSeqs;
+  int32_t* hist = small ? lds_arr : a.scratch;
   int32_t* cnt_gt = hist + nb;
   int32_t* off = cnt_gt + nb;
   int32_t* tie = off + nb;
   int32_t* rank = tie + nb;
-  auto n_tiles_of = [&](int s) {
-    const int L = max(0, a.cu[s + 1] - a.cu[s]);
-    return min(a.max_tiles, (L + a.bm_tok - 1) / a.bm_tok);
-  };
-  if (tid < 64 && a.static_flag) {
-    // max |gamma| of q and k.  Every rotated query row has norm <= sqrt(128)
-    // max|gamma_q| and every rotated key <= sqrt(128) max|gamma_k| (RoPE keeps
-    // norms), so with the query rows pre-scaled by c = scale * log2(e),
-    // |score| <= c * 128 * max|gamma_q| * max|gamma_k|, plus a margin for the
-    // bf16 roundings.  Within 60 (log2 units) every p = 2^score is a normal
-    // float, and the prefill runs its static-bound softmax.
-    const uint16_t* gk = (const uint16_t*)a.k_gamma;
-    const uint16_t* gq = (const uint16_t*)a.q_gamma;
-    float kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * tid])), fabsf(bf16_to_f32(gk[2 * tid + 1])));
-    float qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * tid])), fabsf(bf16_to_f32(gq[2 * tid + 1])));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
-      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
-    }
-    if (tid == 0) a.static_flag[0] = a.scale_log2e * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
-  }
+  int32_t* cu = small ? rank + a.n_seq : nullptr;  // staged offsets (small plans)
+  if (small)
+    for (int i = tid; i <= a.n_seq; i += 1024) cu[i] = a.cu[i];
   for (int i = tid; i < nb; i += 1024) { hist[i] = 0; tie[i] = 0; }
   __syncthreads();
+  auto cu_at = [&](int i) { return small ? cu[i] : a.cu[i]; };
+  auto n_tiles_of = [&](int s) {
+    const int L = max(0, cu_at(s + 1) - cu_at(s));
+    return min(a.max_tiles, (L + a.bm_tok - 1) / a.bm_tok);
+  };
   for (int s = tid; s < a.n_seq; s += 1024) atomicAdd(&hist[n_tiles_of(s)], 1);
   __syncthreads();
   // two suffix sums, 1024 entries at a time from the top (thread order runs
@@ -616,15 +608,36 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
     rank[s] = cnt_gt[nt] + atomicAdd(&tie[nt], 1);
   }
   __syncthreads();
+  if (tid >= 960 && a.static_flag) {
+    // (the last wave, while the others write the list) max |gamma| of q and
+    // k.  Every rotated query row has norm <= sqrt(128) max|gamma_q| and every
+    // rotated key <= sqrt(128) max|gamma_k| (RoPE keeps norms), so with the
+    // query rows pre-scaled by c = scale * log2(e), |score| <= c * 128 *
+    // max|gamma_q| * max|gamma_k|, plus a margin for the bf16 roundings.
+    // Within 60 (log2 units) every p = 2^score is a normal float, and the
+    // prefill runs its static-bound softmax.
+    const int l = tid - 960;
+    const uint16_t* gk = (const uint16_t*)a.k_gamma;
+    const uint16_t* gq = (const uint16_t*)a.q_gamma;
+    float kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * l])), fabsf(bf16_to_f32(gk[2 * l + 1])));
+    float qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * l])), fabsf(bf16_to_f32(gq[2 * l + 1])));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
+      qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
+    }
+    if (l == 0) a.static_flag[0] = a.scale_log2e * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+  }
   for (int s = 0; s < a.n_seq; ++s) {
     const int nt = n_tiles_of(s);
     const int rk = rank[s];
+    const int seq0 = cu_at(s), len = cu_at(s + 1) - seq0;
+    const int p0 = a.start_pos ? a.start_pos[s] : 0;
     for (int q = tid; q < nt; q += 1024) {
       const int pos = off[q] + rk;
       if (pos < a.n_items) {
         PrefillItem it;
-        it.s = s; it.qt = q; it.seq0 = a.cu[s]; it.len = a.cu[s + 1] - a.cu[s];
-        it.p0 = a.start_pos ? a.start_pos[s] : 0;
+        it.s = s; it.qt = q; it.seq0 = seq0; it.len = len; it.p0 = p0;
         it.pad0 = it.pad1 = it.pad2 = 0;
         a.items[pos] = it;
       }

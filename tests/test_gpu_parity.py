@@ -223,6 +223,20 @@ def test_prefill_online_softmax_path():
             assert torch.equal(out_t[cu[s], t], U.up(x["v"][cu[s], t // 4], torch.bfloat16))
 
 
+def test_prefill_many_short_sequences():
+    """2100 packed sequences of 0..9 tokens: the plan kernel's large-plan path
+    (more sequences than its LDS arrays hold), empty sequences included."""
+    rng = np.random.default_rng(123)
+    lengths = rng.integers(0, 10, size=2100).tolist()
+    spec = inputs.custom_spec(123, "bf16", 8, 2, lengths)
+    x = inputs.prefill_inputs(spec)
+    U.say(f"prefill with {len(lengths)} short sequences ({sum(lengths)} tokens)")
+    out = U.down(U.run_prefill(spec, x))
+    ref = oracle.attention_prefill(x["q"], x["k"], x["v"], x["q_gamma"], x["k_gamma"], x["cu_seqlens"], 8, 2,
+                                   eps=spec.eps, theta=spec.theta)
+    print(U.bf16_gate(out, ref, spec, label="many short sequences"))
+
+
 @pytest.mark.parametrize("case_id", [1, 3, 4])
 def test_prefill_full_size_sampled(case_id):
     """Full-size standard workloads in the benchmark's launch configuration;
