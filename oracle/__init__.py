@@ -1,6 +1,8 @@
 """CPU oracle for the Qwen3 attention-sublayer core: QK-Norm, rotate-half RoPE,
 causal grouped-query softmax attention (prefill over packed sequences, and
-appending new tokens against a cache of already-normed, already-rotated keys).
+appending new tokens against a cache of already-normed, already-rotated keys);
+and (``oracle.gated``) the gated global-attention layer of Qwen3-Next /
+Qwen3.5: zero-centred norm, partial RoPE, per-head sigmoid output gate.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -26,4 +28,14 @@ from .attention import (  # noqa: F401
     attention_prefill_rows,
     attention_append,
     attention_decode,
+)
+from .gated import (  # noqa: F401
+    rotary_dim,
+    rms_norm_zero_centred,
+    rope_partial,
+    gated_qk_norm_rope,
+    split_query_gate,
+    sigmoid,
+    gated_attention_prefill,
+    gated_attention_append,
 )

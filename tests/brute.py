@@ -50,3 +50,49 @@ def prefill(q, k, v, q_gamma, k_gamma, lengths, n_q_heads, n_kv_heads, eps, thet
             out.append(row)
         base += L
     return out
+
+
+def _norm_row_zero_centred(row, w, eps):
+    ms = sum(x * x for x in row) / len(row)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [row[i] * r * (1.0 + w[i]) for i in range(len(row))]
+
+
+def _rope_row_partial(row, pos, theta, rot):
+    out = list(row)
+    h = rot // 2
+    for i in range(h):
+        ang = pos * theta ** (-(2.0 * i) / rot)
+        c, s = math.cos(ang), math.sin(ang)
+        out[i] = row[i] * c - row[i + h] * s
+        out[i + h] = row[i + h] * c + row[i] * s
+    return out
+
+
+def gated_prefill(q, gate, k, v, q_w, k_w, lengths, n_q_heads, n_kv_heads, eps, theta, rot):
+    """The gated global-attention layer: zero-centred norm (scale 1 + w), RoPE on
+    the first ``rot`` coordinates with frequency theta^(-2i/rot), causal GQA
+    softmax attention, output times 1 / (1 + exp(-gate))."""
+    g = n_q_heads // n_kv_heads
+    d = len(q[0][0])
+    scale = 1.0 / math.sqrt(d)
+    out = []
+    base = 0
+    for L in lengths:
+        qh = [[_rope_row_partial(_norm_row_zero_centred(q[base + i][t], q_w, eps), i, theta, rot)
+               for t in range(n_q_heads)] for i in range(L)]
+        kh = [[_rope_row_partial(_norm_row_zero_centred(k[base + j][u], k_w, eps), j, theta, rot)
+               for u in range(n_kv_heads)] for j in range(L)]
+        for i in range(L):
+            row = []
+            for t in range(n_q_heads):
+                u = t // g
+                s = [sum(qh[i][t][e] * kh[j][u][e] for e in range(d)) * scale for j in range(i + 1)]
+                m = max(s)
+                wts = [math.exp(x - m) for x in s]
+                z = sum(wts)
+                row.append([sum(wts[j] * v[base + j][u][e] for j in range(i + 1)) / z
+                            / (1.0 + math.exp(-gate[base + i][t][e])) for e in range(d)])
+            out.append(row)
+        base += L
+    return out

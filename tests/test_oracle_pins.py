@@ -124,3 +124,70 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     except (AssertionError, ValueError):
         failed.append("pin_brute_force_d128")
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------------------ gated global-attention layer
+
+import pins_gated  # noqa: E402
+from oracle import gated as G  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", pins_gated.GATED_PINS, ids=lambda f: f.__name__)
+def test_gated_pin(pin):
+    pin()
+
+
+def test_gated_brute_force_full_width():
+    pins_gated.pin_gated_brute_force(d=32, rot=8)
+
+
+def _rope_partial_full_denominator(x, positions, theta, rot_dim):
+    # frequency denominator head_dim instead of rot_dim (the proportional-RoPE convention)
+    x = np.asarray(x, dtype=np.float64)
+    d, h = x.shape[-1], rot_dim // 2
+    inv = np.power(float(theta), -(2.0 * np.arange(h)) / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :h], x[..., h:rot_dim]
+    return np.concatenate([a * c - b * s, b * c + a * s, x[..., rot_dim:]], axis=-1)
+
+
+def _rope_partial_all_dims(x, positions, theta, rot_dim):
+    return A.rope_rotate_half(x, positions, theta)
+
+
+def _norm_plain_gamma(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(w)
+
+
+def _split_halves(q_proj_out, n_heads, head_dim):
+    y = np.asarray(q_proj_out, dtype=np.float64).reshape(-1, 2 * n_heads * head_dim)
+    return (y[:, :n_heads * head_dim].reshape(-1, n_heads, head_dim),
+            y[:, n_heads * head_dim:].reshape(-1, n_heads, head_dim))
+
+
+def _sigmoid_tanh(x):
+    return np.tanh(np.asarray(x, dtype=np.float64))
+
+
+GATED_MUTATIONS = {
+    "rope_full_denominator": ("rope_partial", _rope_partial_full_denominator),
+    "rope_all_dims": ("rope_partial", _rope_partial_all_dims),
+    "norm_gamma_not_one_plus_w": ("rms_norm_zero_centred", _norm_plain_gamma),
+    "gate_split_across_heads": ("split_query_gate", _split_halves),
+    "gate_tanh": ("sigmoid", _sigmoid_tanh),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATED_MUTATIONS))
+def test_gated_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = GATED_MUTATIONS[name]
+    monkeypatch.setattr(G, attr, fn)
+    failed = []
+    for pin in pins_gated.GATED_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
