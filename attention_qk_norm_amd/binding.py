@@ -17,12 +17,14 @@ _lib = None
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, BF16 = 0, 1
 HEAD_DIM = 128
+HEAD_DIM_GATED = 256
 
 
 class Params(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("rotary_dim", ctypes.c_int32), ("norm_offset", ctypes.c_float),
+                ("output_gate", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -79,8 +81,25 @@ def load(path=None):
     return lib
 
 
-def make_params(n_q_heads, n_kv_heads, eps=1e-6, rope_theta=1e6, softmax_scale=0.0, head_dim=HEAD_DIM, order=0):
-    return Params(n_q_heads, n_kv_heads, head_dim, eps, rope_theta, softmax_scale, order)
+def make_params(n_q_heads, n_kv_heads, eps=1e-6, rope_theta=1e6, softmax_scale=0.0, head_dim=HEAD_DIM, order=0,
+                rotary_dim=0, norm_offset=0.0, output_gate=0):
+    return Params(n_q_heads, n_kv_heads, head_dim, eps, rope_theta, softmax_scale, order, rotary_dim, norm_offset,
+                  output_gate)
+
+
+def make_gated_params(n_q_heads, n_kv_heads, eps=1e-6, rope_theta=1e7, rotary_dim=64, softmax_scale=0.0, order=0,
+                      output_gate=1):
+    """A gated global-attention layer (Qwen3-Next / Qwen3.5): head_dim 256,
+    zero-centred QK-Norm, partial RoPE, per-head sigmoid output gate."""
+    return make_params(n_q_heads, n_kv_heads, eps=eps, rope_theta=rope_theta, softmax_scale=softmax_scale,
+                       head_dim=HEAD_DIM_GATED, order=order, rotary_dim=rotary_dim, norm_offset=1.0,
+                       output_gate=output_gate)
+
+
+def _out_like(params, q):
+    """Output tensor for a call whose queries are q (q carries the gate halves
+    when params.output_gate is set)."""
+    return torch.empty(q.shape[0], params.n_q_heads, params.head_dim, dtype=q.dtype, device=q.device)
 
 
 def _check(status):
@@ -111,26 +130,27 @@ def _stream():
 
 
 def cache_desc(k_cache):
-    """Descriptor of a [n_seq][n_kv_heads][capacity][128] cache tensor (strides may vary)."""
+    """Descriptor of a [n_seq][n_kv_heads][capacity][head_dim] cache tensor (strides may vary)."""
     s = k_cache.stride()
     return CacheDesc(s[0], s[1], s[2], k_cache.shape[2])
 
 
-def _check_cache_pair(k_cache, v_cache):
+def _check_cache_pair(params, k_cache, v_cache):
     if v_cache is None or k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must share one shape and stride layout")
-    if k_cache.dim() != 4 or k_cache.shape[3] != HEAD_DIM or k_cache.stride(3) != 1:
-        raise ValueError("cache must be [n_seq][n_kv_heads][capacity][128] with the last dim contiguous")
+    if k_cache.dim() != 4 or k_cache.shape[3] != params.head_dim or k_cache.stride(3) != 1:
+        raise ValueError("cache must be [n_seq][n_kv_heads][capacity][head_dim] with the last dim contiguous")
 
 
 def qk_norm_rope(params, q, k, q_gamma, k_gamma, positions, q_out=None, k_out=None):
-    """QK-Norm then RoPE of q [n_tok, Hq, 128] and/or k [n_tok, Hkv, 128] at ``positions``."""
+    """QK-Norm then RoPE of q [n_tok, Hq, d] (gated: [n_tok, Hq, 2d]) and/or
+    k [n_tok, Hkv, d] at ``positions``."""
     lib = load()
     ref = q if q is not None else k
     for t, n in ((q, "q"), (k, "k"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"), (positions, "positions")):
         _dev(t, n)
     if q is not None and q_out is None:
-        q_out = torch.empty_like(q)
+        q_out = _out_like(params, q)
     if k is not None and k_out is None:
         k_out = torch.empty_like(k)
     n_tok = ref.shape[0]
@@ -179,10 +199,10 @@ def prefill(params, q, k, v, q_gamma, k_gamma, cu_seqlens, cu_seqlens_host=None,
     max_len = int((cu_h[1:] - cu_h[:-1]).max()) if n_seq > 0 else 0
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
+        out = _out_like(params, q)
     desc = None
     if k_cache is not None:
-        _check_cache_pair(k_cache, v_cache)
+        _check_cache_pair(params, k_cache, v_cache)
         desc = cache_desc(k_cache)
     nbytes = prefill_workspace_size(params, dt, n_seq, n_tok, max_len, k_cache is not None)
     ws = _workspace(nbytes, q.device, workspace)
@@ -217,8 +237,8 @@ def append(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, cu_ne
     max_new = int((cu_h[1:] - cu_h[:-1]).max()) if n_seq > 0 else 0
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
-    _check_cache_pair(k_cache, v_cache)
+        out = _out_like(params, q)
+    _check_cache_pair(params, k_cache, v_cache)
     desc = cache_desc(k_cache)
     nbytes = append_workspace_size(params, dt, n_seq, n_new, max_new)
     ws = _workspace(nbytes, q.device, workspace)
@@ -245,8 +265,8 @@ def decode(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, start
     n_seq = sp_h.numel()
     dt = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
-    _check_cache_pair(k_cache, v_cache)
+        out = _out_like(params, q)
+    _check_cache_pair(params, k_cache, v_cache)
     desc = cache_desc(k_cache)
     nbytes = decode_workspace_size(params, dt, n_seq, int(sp_h.sum()))
     ws = _workspace(nbytes, q.device, workspace)

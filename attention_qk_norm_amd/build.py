@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qwattn_api.cpp", "k_normrope.hip", "k_prefill.hip", "k_attn_f32.hip", "k_decode.hip"]
+SOURCES = ["qwattn_api.cpp", "k_normrope.hip", "k_prefill.hip", "k_prefill_wide.hip", "k_attn_f32.hip", "k_decode.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code (the host pass of
 # hipcc warns that it does not know the feature; that is harmless).
@@ -27,10 +27,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
-# arch VGPRs: its softmax reads every score with VALU, and the AGPR form made
+# Per-source extra flags.  The prefill kernels keep their MFMA accumulators in
+# arch VGPRs: the softmax reads every score with VALU, and the AGPR form made
 # the compiler shuttle the query fragments and scores between register files.
-SOURCE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "k_prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, objdir, extra=()):

@@ -5,12 +5,14 @@
 
 namespace qw {
 
-constexpr int kD = 128;       // head_dim (the only one supported)
-constexpr int kHalf = kD / 2; // RoPE pairs (i, i + 64)
+constexpr int kD = 128;       // head_dim of the Qwen3 layers
+constexpr int kHalf = kD / 2; // their RoPE pairs (i, i + 64)
+constexpr int kMaxD = 256;    // head_dim of the gated (Qwen3-Next / Qwen3.5) layers
 
-// RoPE frequencies theta^(-2i/128), i < 64, computed by the host in double.
+// RoPE frequencies theta^(-2i/rot), i < rot/2 (rot = the rotated coordinates,
+// the whole head for Qwen3), computed by the host in double.
 struct RopeFreq {
-  double w[kHalf];
+  double w[kMaxD / 2];
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

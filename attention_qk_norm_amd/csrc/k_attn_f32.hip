@@ -6,10 +6,12 @@
 // Queries arrive already normed and rotated (fp32, from the norm+RoPE pass);
 // keys already normed and rotated (cache or workspace).  A workgroup owns one
 // (sequence, KV head) and up to 64 query rows = tokens x the g heads of the
-// group; four lanes share a row, each holding 32 of its dims, so a score is 32
-// FMAs plus a 4-lane reduction.  32-key K and V tiles are staged in LDS and read
-// as broadcasts.  Online softmax in fp32 (exp2 with log2(e) folded into the
-// scale).  Decode mode: one query token per sequence at start_pos, keys
+// group; four lanes share a row, each holding a quarter of its dims (32 of 128,
+// or 64 of 256), so a score is that many FMAs plus a 4-lane reduction.  K and V
+// tiles (32 keys at head_dim 128, 16 at 256) are staged in LDS and read as
+// broadcasts.  Online softmax in fp32 (exp2 with log2(e) folded into the
+// scale); the gated layers ("第 20 章 Qwen3 与 Qwen3.5" §20.4) then multiply
+// each output row by sigmoid of its gate row.  Decode mode: one query token per sequence at start_pos, keys
 // 0 .. start_pos of the cache (the new key already appended).  Prefill mode
 // with start_pos set (an append): sequence s's rows are new tokens at
 // start_pos[s] .., attending to cache slots 0 .. their own position.
@@ -18,11 +20,12 @@
 namespace qw {
 namespace {
 
-constexpr int kKeys = 32;
-
+template <int D>
 __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) float kt[kKeys][kD];
-  __shared__ __attribute__((aligned(16))) float vt[kKeys][kD];
+  constexpr int kKeys = 4096 / D;  // keys per LDS tile
+  constexpr int DPL = D / 4;       // dims per lane
+  __shared__ __attribute__((aligned(16))) float kt[kKeys][D];
+  __shared__ __attribute__((aligned(16))) float vt[kKeys][D];
 
   const int tid = threadIdx.x;
   const int u = blockIdx.x % a.Hkv;
@@ -57,20 +60,20 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
   const int qpos = valid ? pos0 + qtok : 0x3fffffff;
   const int t_head = u * a.g + hoff;
 
-  float q[32], o[32];
+  float q[DPL], o[DPL];
   if (valid) {
-    const float* src = (const float*)a.qhat + ((int64_t)(row_base + qtok) * a.Hq + t_head) * kD + 32 * sub;
+    const float* src = (const float*)a.qhat + ((int64_t)(row_base + qtok) * a.Hq + t_head) * D + DPL * sub;
 #pragma unroll
-    for (int e = 0; e < 32; e += 4) {
+    for (int e = 0; e < DPL; e += 4) {
       f32x4 x = *reinterpret_cast<const f32x4*>(src + e);
       q[e] = x[0]; q[e + 1] = x[1]; q[e + 2] = x[2]; q[e + 3] = x[3];
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) q[e] = 0.f;
+    for (int e = 0; e < DPL; ++e) q[e] = 0.f;
   }
 #pragma unroll
-  for (int e = 0; e < 32; ++e) o[e] = 0.f;
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
   const float* kbase = (const float*)a.khat + u * a.ks_head +
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {  // 1024 16-byte chunks per tile and tensor
       const int c = tid + 256 * m;
-      const int row = c >> 5, col = (c & 31) * 4;
+      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
       const int key = k0 + row;
       f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
       if (key < n_kv) {
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
     for (int j = 0; j < kKeys; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc = fmaf(q[e], kt[j][32 * sub + e], acc);
+      for (int e = 0; e < DPL; ++e) acc = fmaf(q[e], kt[j][DPL * sub + e], acc);
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
       float x = acc * a.scale_log2e;
@@ -114,23 +117,30 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) o[e] *= alpha;
+    for (int e = 0; e < DPL; ++e) o[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const float p = exp2f(sc[j] - m_new);
       psum += p;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) o[e] = fmaf(p, vt[j][32 * sub + e], o[e]);
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(p, vt[j][DPL * sub + e], o[e]);
     }
     l_run = l_run * alpha + psum;
   }
 
   if (valid) {
     const float inv_l = 1.0f / l_run;
-    float* dst = (float*)a.out + ((int64_t)(row_base + qtok) * a.Hq + t_head) * kD + 32 * sub;
+    const int64_t row = (int64_t)(row_base + qtok) * a.Hq + t_head;
+    float* dst = (float*)a.out + row * D + DPL * sub;
+    const float* gp = a.gate ? (const float*)a.gate + row * a.q_row + DPL * sub : nullptr;
 #pragma unroll
-    for (int e = 0; e < 32; e += 4) {
+    for (int e = 0; e < DPL; e += 4) {
       f32x4 x = {o[e] * inv_l, o[e + 1] * inv_l, o[e + 2] * inv_l, o[e + 3] * inv_l};
+      if (gp) {
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(gp + e);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] /= 1.0f + expf(-gv[c]);
+      }
       *reinterpret_cast<f32x4*>(dst + e) = x;
     }
   }
@@ -141,7 +151,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(PrefillArgs a) {
 hipError_t launch_attn_f32(const PrefillArgs& a, int n_items, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (a.head_dim == kMaxD)
+    hipLaunchKernelGGL(k_attn_f32<kMaxD>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_attn_f32<kD>, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

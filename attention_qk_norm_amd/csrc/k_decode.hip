@@ -1,12 +1,12 @@
-// Split-K decode over a bf16 KV cache (HBM-bound).
+// Split-K decode over a bf16 KV cache (HBM-bound), head_dim 128 or 256.
 //
 // One new query token per sequence attends to the cache slots 0 .. start_pos[i]
 // of its KV head, the new key having been normed, rotated at start_pos and
 // appended by the prologue ("第 20 章 Qwen3 与 Qwen3.5" §20.3: only the new K is
 // rotated; cached keys already carry their rotation).  The key axis of every
 // (sequence, KV head) is cut into chunks; a workgroup streams one chunk, its four
-// waves taking interleaved 32-key blocks, and leaves a partial (m, l, acc[128])
-// per query head.  A second kernel merges the partials with the exact softmax
+// waves taking interleaved 32-key blocks, and leaves a partial (m, l,
+// acc[head_dim]) per query head.  A second kernel merges the partials with the exact softmax
 // identity o = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
 //
 // Per 32-key block a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
@@ -15,24 +15,34 @@
 // the softmax is lane-local plus two lane swaps.  The probabilities, rounded to
 // bf16, are the B operand of O^T = V^T P^T; V goes HBM -> registers -> the
 // wave's own LDS slot and comes back transposed through ds_read_b64_tr_b16.
-// Every K and V byte is read once, in 16-byte lane loads.
+// Every K and V byte is read once, in 16-byte lane loads.  The gated layers
+// ("第 20 章 Qwen3 与 Qwen3.5" §20.4) multiply the merged output by sigmoid of
+// the gate in the merge kernel.
 #include "kernels.h"
 
 namespace qw {
 namespace {
 
 constexpr int kBlockKeys = 32;
-constexpr int kRowBytes = kD * 2;
 
-// V block in LDS: 32 rows x 256 B.  The transposed reads of one half-wave touch
-// 8 rows x 32 bytes; XOR-ing the 16-byte chunk with (row & 7) << 1 spreads those
-// 8 rows over the 8 32-byte windows of a 256-byte bank line.
+// V block in LDS: 32 rows x 2D bytes.  The transposed reads of one half-wave
+// touch 8 rows x 32 bytes; XOR-ing the 16-byte chunk with (row & 7) << 1 spreads
+// those 8 rows over the 8 32-byte windows of a 256-byte bank line.
+template <int D>
 __device__ __forceinline__ int v_swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ ((row & 7) << 1)) << 4);
+  return row * (2 * D) + ((chunk ^ ((row & 7) << 1)) << 4);
 }
 
+// Dynamic LDS: the four waves' V blocks, later reused for the merge.
+template <int D>
+constexpr int decode_smem_bytes() {
+  return 4 * kBlockKeys * 2 * D + 4 * 2 * 16 * 4;
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kBlockKeys * kRowBytes + 4 * 2 * 16 * 4];
+  constexpr int KF = D / 32;  // K / Q fragments per 16 x 32-dim slice row
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int u = blockIdx.x % a.Hkv;
   const int cg = blockIdx.x / a.Hkv;
@@ -46,22 +56,22 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   const bool hvalid = hh < a.g;
 
   // query fragments: B[k = dim 32kk + 8q4 + e][n = head hh]
-  bf16x8 qf[4];
+  bf16x8 qf[KF];
   {
-    const uint16_t* src = a.qhat + ((int64_t)i * a.Hq + u * a.g + (hvalid ? hh : 0)) * kD + 8 * q4;
+    const uint16_t* src = a.qhat + ((int64_t)i * a.Hq + u * a.g + (hvalid ? hh : 0)) * D + 8 * q4;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KF; ++kk) {
       u32x4 raw = hvalid ? *reinterpret_cast<const u32x4*>(src + 32 * kk) : u32x4{0, 0, 0, 0};
       qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
   const uint16_t* kb = a.k_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
   const uint16_t* vb = a.v_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
-  lds_u8* vs = (lds_u8*)(smem) + w * kBlockKeys * kRowBytes;
+  lds_u8* vs = (lds_u8*)(smem) + w * kBlockKeys * 2 * D;
 
-  f32x4 o[8];
+  f32x4 o[D / 16];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -1e30f, l_run = 0.f;
 
   // transposed-read coordinates: group q4 reads rows 4 q4 + (lam >> 2) (+16)
@@ -71,22 +81,23 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 
   for (int b0 = kbeg + w * kBlockKeys; b0 < kend; b0 += 4 * kBlockKeys) {
     // K fragments: A[m = key b0 + 16 sb + hh][k = dim 32kk + 8 q4 + e]
-    u32x4 kr[2][4];
+    u32x4 kr[2][KF];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int key = b0 + 16 * sb + hh;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < KF; ++kk)
         kr[sb][kk] = key < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * a.cs_tok + 32 * kk + 8 * q4)
                                 : u32x4{0, 0, 0, 0};
     }
-    // V rows of the block: lane chunk c = lane + 64 m -> row c / 16, 16-byte chunk c % 16
-    u32x4 vr[8];
+    // V rows of the block: lane chunk c = lane + 64 m -> row c / (D/8), 16-byte chunk c % (D/8)
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    u32x4 vr[D / 16];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < D / 16; ++m) {
       const int c = lane + 64 * m;
-      const int key = b0 + (c >> 4);
-      vr[m] = key < kend ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * a.cs_tok + (c & 15) * 8)
+      const int key = b0 + c / CPR;
+      vr[m] = key < kend ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * a.cs_tok + (c % CPR) * 8)
                          : u32x4{0, 0, 0, 0};
     }
     f32x4 sacc[2];
@@ -94,16 +105,16 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     for (int sb = 0; sb < 2; ++sb) {
       sacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < KF; ++kk)
         sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[sb][kk]), qf[kk],
                                                           sacc[sb], 0, 0, 0);
     }
     // stage V in this wave's LDS slot (only this wave reads it)
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < D / 16; ++m) {
       const int c = lane + 64 * m;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vs + v_swz(c >> 4, c & 15)) = vr[m];
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vs + v_swz<D>(c / CPR, c % CPR)) = vr[m];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -138,11 +149,11 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 
     // O^T[d][head] += V^T[d][keys] P^T[keys][head]
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < D / 16; ++db) {
       const int col = 16 * db + v_col;
       const int off = (col & 7) * 2;
-      const bf16x8 va = concat_tr16(lds_read_tr16(vs + v_swz(v_row, col >> 3) + off),
-                                    lds_read_tr16(vs + v_swz(v_row + 16, col >> 3) + off));
+      const bf16x8 va = concat_tr16(lds_read_tr16(vs + v_swz<D>(v_row, col >> 3) + off),
+                                    lds_read_tr16(vs + v_swz<D>(v_row + 16, col >> 3) + off));
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[db][j] *= alpha;
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, o[db], 0, 0, 0);
@@ -153,19 +164,19 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   __syncthreads();
-  float* ob = reinterpret_cast<float*>(smem);           // [4 waves][16 heads][128 d]
-  float* ml = ob + 4 * 16 * kD;                          // [4 waves][2][16]
+  float* ob = reinterpret_cast<float*>(smem);           // [4 waves][16 heads][D]
+  float* ml = ob + 4 * 16 * D;                           // [4 waves][2][16]
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ob[(w * 16 + hh) * kD + 16 * db + 4 * q4 + j] = o[db][j];
+    for (int j = 0; j < 4; ++j) ob[(w * 16 + hh) * D + 16 * db + 4 * q4 + j] = o[db][j];
   if (q4 == 0) {
     ml[(w * 2 + 0) * 16 + hh] = m_run;
     ml[(w * 2 + 1) * 16 + hh] = l_run;
   }
   __syncthreads();
-  for (int e = tid; e < a.g * kD; e += 256) {
-    const int h = e / kD, d = e % kD;
+  for (int e = tid; e < a.g * D; e += 256) {
+    const int h = e / D, d = e % D;
     float M = -1e30f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, ml[(ww * 2) * 16 + h]);
@@ -173,42 +184,56 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const float f = __builtin_amdgcn_exp2f(ml[(ww * 2) * 16 + h] - M);
-      acc += f * ob[(ww * 16 + h) * kD + d];
+      acc += f * ob[(ww * 16 + h) * D + d];
       lsum += f * ml[(ww * 2 + 1) * 16 + h];
     }
-    float* dst = a.partial + ((int64_t)cg * a.Hq + u * a.g + h) * kPartStride;
+    float* dst = a.partial + ((int64_t)cg * a.Hq + u * a.g + h) * (D + 4);
     dst[d] = acc;
     if (d == 0) {
-      dst[kD] = M;
-      dst[kD + 1] = lsum;
+      dst[D] = M;
+      dst[D + 1] = lsum;
     }
   }
 }
 
 // One wave per (sequence, query head): merge its chunks' partials.  The lanes
 // first take the chunks' maxima in parallel; the weighted sum then walks the
-// chunks with four loads in flight, each lane owning two of the 128 dims.
+// chunks with four loads in flight, each lane owning D/64 of the dims.
+template <int D>
 __global__ __launch_bounds__(64) void k_decode_combine(DecodeArgs a) {
+  constexpr int N = D / 64;
   const int i = blockIdx.x / a.Hq, t = blockIdx.x % a.Hq;
   const int lane = threadIdx.x;
   const int c0 = a.chunk_off[i], c1 = a.chunk_off[i + 1];
-  const float* base = a.partial + t * kPartStride;
-  const int64_t cstride = (int64_t)a.Hq * kPartStride;
+  const float* base = a.partial + t * (D + 4);
+  const int64_t cstride = (int64_t)a.Hq * (D + 4);
   float M = -1e30f;
-  for (int c = c0 + lane; c < c1; c += 64) M = fmaxf(M, base[c * cstride + kD]);
+  for (int c = c0 + lane; c < c1; c += 64) M = fmaxf(M, base[c * cstride + D]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+  float acc[N], lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) acc[e] = 0.f;
 #pragma unroll 4
   for (int c = c0; c < c1; ++c) {
     const float* p = base + c * cstride;
-    const float f = __builtin_amdgcn_exp2f(p[kD] - M);
-    lsum += f * p[kD + 1];
-    acc0 += f * p[2 * lane];
-    acc1 += f * p[2 * lane + 1];
+    const float f = __builtin_amdgcn_exp2f(p[D] - M);
+    lsum += f * p[D + 1];
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc[e] += f * p[N * lane + e];
   }
   const float inv = 1.0f / lsum;
-  *reinterpret_cast<uint32_t*>(a.out + ((int64_t)i * a.Hq + t) * kD + 2 * lane) = pack_bf16x2(acc0 * inv, acc1 * inv);
+  float y[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) y[e] = acc[e] * inv;
+  if (a.gate) {  // gated layers: times sigmoid(gate) at the same dims
+    const uint16_t* gp = a.gate + ((int64_t)i * a.Hq + t) * a.q_row + N * lane;
+#pragma unroll
+    for (int e = 0; e < N; ++e) y[e] /= 1.0f + __expf(-bf16_to_f32(gp[e]));
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + ((int64_t)i * a.Hq + t) * D + N * lane);
+#pragma unroll
+  for (int e = 0; e < N / 2; ++e) dst[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
 }
 
 // chunk_off[i] = sum_{i' < i} ceil((start_pos[i'] + 1) / chunk); one workgroup.
@@ -245,13 +270,26 @@ hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, in
 
 hipError_t launch_decode_split(const DecodeArgs& a, int total_chunks, hipStream_t st) {
   if (total_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_split, dim3((unsigned)((int64_t)total_chunks * a.Hkv)), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((int64_t)total_chunks * a.Hkv));
+  if (a.head_dim == kMaxD) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)k_decode_split<kMaxD>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       decode_smem_bytes<kMaxD>());
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(k_decode_split<kMaxD>, grid, dim3(256), decode_smem_bytes<kMaxD>(), st, a);
+  } else {
+    hipLaunchKernelGGL(k_decode_split<kD>, grid, dim3(256), decode_smem_bytes<kD>(), st, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st) {
   if (a.n_seq <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_combine, dim3((unsigned)((int64_t)a.n_seq * a.Hq)), dim3(64), 0, st, a);
+  const dim3 grid((unsigned)((int64_t)a.n_seq * a.Hq));
+  if (a.head_dim == kMaxD)
+    hipLaunchKernelGGL(k_decode_combine<kMaxD>, grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_decode_combine<kD>, grid, dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -609,24 +609,29 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
   }
   __syncthreads();
   if (tid >= 960 && a.static_flag) {
-    // (the last wave, while the others write the list) max |gamma| of q and
-    // k.  Every rotated query row has norm <= sqrt(128) max|gamma_q| and every
-    // rotated key <= sqrt(128) max|gamma_k| (RoPE keeps norms), so with the
-    // query rows pre-scaled by c = scale * log2(e), |score| <= c * 128 *
-    // max|gamma_q| * max|gamma_k|, plus a margin for the bf16 roundings.
-    // Within 60 (log2 units) every p = 2^score is a normal float, and the
-    // prefill runs its static-bound softmax.
+    // (the last wave, while the others write the list) the largest norm scale
+    // |gamma_offset + gamma| of q and of k.  Every rotated query row has norm
+    // <= sqrt(d) times the q maximum and every rotated key <= sqrt(d) times the
+    // k maximum (the normed row has RMS 1 and RoPE keeps norms), so with the
+    // query rows pre-scaled by c = scale * log2(e), |score| <= c * d * max_q *
+    // max_k, plus a margin for the bf16 roundings.  Within 60 (log2 units)
+    // every p = 2^score is a normal float, and the prefill runs its
+    // static-bound softmax.
     const int l = tid - 960;
     const uint16_t* gk = (const uint16_t*)a.k_gamma;
     const uint16_t* gq = (const uint16_t*)a.q_gamma;
-    float kmax = fmaxf(fabsf(bf16_to_f32(gk[2 * l])), fabsf(bf16_to_f32(gk[2 * l + 1])));
-    float qmax = fmaxf(fabsf(bf16_to_f32(gq[2 * l])), fabsf(bf16_to_f32(gq[2 * l + 1])));
+    float kmax = 0.f, qmax = 0.f;
+    for (int i = l; i < a.head_dim; i += 64) {
+      kmax = fmaxf(kmax, fabsf(a.gamma_offset + bf16_to_f32(gk[i])));
+      qmax = fmaxf(qmax, fabsf(a.gamma_offset + bf16_to_f32(gq[i])));
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
       qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
     }
-    if (l == 0) a.static_flag[0] = a.scale_log2e * 128.f * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+    if (l == 0)
+      a.static_flag[0] = a.scale_log2e * (float)a.head_dim * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
   }
   for (int s = 0; s < a.n_seq; ++s) {
     const int nt = n_tiles_of(s);

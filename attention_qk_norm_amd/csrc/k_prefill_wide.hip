@@ -1,0 +1,374 @@
+// Causal grouped-query attention prefill at head_dim 256 (the gated global
+// layers of Qwen3-Next / Qwen3.5), bf16 in / fp32 math, MFMA on gfx950.
+//
+// What it computes ("14. Qwen 家族：从 QKV 偏置到混合注意力", section on
+// Qwen3-Next; "第 20 章 Qwen3 与 Qwen3.5" §20.4): for query head t and its KV head
+// u = floor(t / g), o_i = sigmoid(gate_i) * sum_j softmax_j(q_i . k_j / sqrt(256)) v_j
+// over keys j <= i of the same sequence.  q is normed with the scale
+// norm_offset + gamma (1 + w for the zero-centred norm) and rotated on its first
+// `rot` coordinates only (pairs (i, i + rot/2), frequency theta^(-2i/rot)); this
+// happens here, in the prologue.  k arrives normed and rotated the same way (the
+// norm+RoPE pass wrote it to the cache or the workspace).  Without a gate the
+// output is the plain attention.
+//
+// Work layout: a workgroup (4 waves, one per SIMD) owns one KV head u of one
+// sequence and a query tile of bm_tok tokens x g heads = up to 128 rows; every
+// K/V tile staged in LDS serves all g heads of the group.  Each wave holds one
+// 32-row block.  At head_dim 256 a wave's O accumulators (32 rows x 256 dims)
+// and resident Q fragments fill the register file that two 32-row blocks use at
+// head_dim 128, so every LDS fragment read feeds one MFMA here.
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+// (A = a K fragment from LDS, B = the wave's resident bf16 Q fragments): each
+// lane owns one query row (lane % 32) and 16 keys of every 32-key block, so the
+// softmax is lane-local plus one lane-pair exchange, and the probabilities,
+// rounded to bf16, are directly the B operand of O^T = V^T P^T once the key
+// order inside each 16-key slice is permuted the same way on the V side (V^T
+// fragments come from gfx950's transposed LDS read, ds_read_b64_tr_b16).
+//
+// K/V tiles of 64 keys (32 KB each) go HBM -> LDS directly
+// (global_load_lds_dwordx4) into a two-stage ring: tile t+1 lands while tile t
+// is used.
+//
+// Softmax: as in the head_dim-128 kernel, the query rows are pre-multiplied by
+// c = scale * log2(e); when the launch-wide bound c * 256 * max|scale_q| *
+// max|scale_k| (plus a rounding margin) is <= 60, p = 2^score needs no running
+// maximum (the static-bound form, decided by the plan kernel); otherwise the
+// online softmax runs.  The row sum adds the bf16-rounded weights that the PV
+// MFMA uses.
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace qw {
+namespace {
+
+constexpr int kW = 256;          // head_dim
+constexpr int kTileKeys = 64;
+// LDS tile layout: row r of a 64-row tile (512 bytes) lives in 1 KB block
+// r % 32, slot r / 32; blocks are padded apart (K: 1040 B, V: 1088 B).  A direct
+// global->LDS load fills one whole block (lane l -> slot l / 32, 16-byte chunk
+// l % 32).  Consecutive rows then sit in consecutive blocks, so
+//  * K (b128 reads, 16 consecutive rows at one chunk): the 16 B block skew
+//    spreads the 16 rows over the 16 chunk slots of a 256 B bank line;
+//  * V (transposed b64 reads, 4 consecutive rows x 64 B per half-wave): the
+//    64 B skew puts the 4 rows in the 4 windows of a bank line.
+constexpr int kBlocks = 32;
+constexpr int kKBlk = 1040, kVBlk = 1088;
+constexpr int kKTile = kBlocks * kKBlk, kVTile = kBlocks * kVBlk;
+constexpr int kStageBytes = kKTile + kVTile;
+constexpr int kStages = 2;
+constexpr int kSmem = kStages * kStageBytes;
+static_assert(kSmem <= 160 * 1024, "LDS per workgroup");
+constexpr int kBlocksPerWave = kBlocks / 4;  // per tensor and tile
+constexpr float kStaticBoundMax = 60.f;      // log2 units
+
+__device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (lane l's bytes land at
+// lds_base + 16 l; M0 holds the wave-uniform base, one wait state after writing
+// it).  Inline assembly, so the compiler does not put a wait for every
+// outstanding copy in front of each LDS read: the tile loop waits for its own
+// copies (s_waitcnt vmcnt(0)) before the barrier that publishes a tile.
+__device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// QK-Norm and partial RoPE of the lane's half query row (dims 16kk + 8hg + e,
+// kk < 16, e < 8), times c, into bf16 MFMA B fragments (AGPRs).  Dims i and
+// i + ROT/2 of a rotation pair sit in fragments kk and kk + ROT/32 of the same
+// lane; fragments from ROT/16 on pass unrotated.
+template <int ROT>
+__device__ __forceinline__ void q_prologue(const PrefillArgs& a, const u32x4 (&raw)[16], bool ok, int pos, int hg,
+                                           bf16x8 (&frag)[16]) {
+  constexpr int RH = ROT / 32;
+  float x[16][8];
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[kk][2 * e] = ok ? bf16_lo(raw[kk][e]) : 0.f;
+      x[kk][2 * e + 1] = ok ? bf16_hi(raw[kk][e]) : 0.f;
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
+  ss = pair_sum(ss);  // lane l ^ 32 holds the other half of the row
+  const float inv = rsqrtf(ss * (1.0f / kW) + a.eps);
+  const uint16_t* gq = (const uint16_t*)a.q_gamma + 8 * hg;
+  auto scale = [&](int kk) __attribute__((always_inline)) {
+    const u32x4 gr = *reinterpret_cast<const u32x4*>(gq + 16 * kk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[kk][2 * e] *= inv * (a.gamma_offset + bf16_lo(gr[e]));
+      x[kk][2 * e + 1] *= inv * (a.gamma_offset + bf16_hi(gr[e]));
+    }
+  };
+  // RMS is rotation-invariant, so one inv serves both orders; they differ in
+  // whether the norm scale applies before the rotation (order 0) or after it.
+  if (a.order == 0)
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) scale(kk);
+  // The angle p * w_i is reduced in fp64 (whole turns removed exactly) and
+  // evaluated by the hardware sine/cosine, which take turns.
+  const double turn = 0.15915494309189535;  // 1 / (2 pi)
+#pragma unroll
+  for (int kk = 0; kk < RH; ++kk) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i0 = 16 * kk + e;  // angle index of hg = 0; hg = 1 adds 8
+      const double w = hg ? a.rope.w[i0 + 8] : a.rope.w[i0];
+      const double t = (double)pos * (w * turn);
+      const float r = (float)(t - rint(t));
+      const float c = __builtin_amdgcn_cosf(r), s = __builtin_amdgcn_sinf(r);
+      const float y1 = x[kk][e], y2 = x[kk + RH][e];
+      x[kk][e] = y1 * c - y2 * s;
+      x[kk + RH][e] = y2 * c + y1 * s;
+    }
+  }
+  if (a.order != 0)
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) scale(kk);
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    u32x4 w4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t v = pack_bf16x2(x[kk][2 * e] * a.scale_log2e, x[kk][2 * e + 1] * a.scale_log2e);
+      asm("v_accvgpr_write_b32 %0, %1" : "=a"(w4[e]) : "v"(v));
+    }
+    frag[kk] = __builtin_bit_cast(bf16x8, w4);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kStages x (K, V)
+  lds_u8* lds = (lds_u8*)(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  // Consecutive workgroups take the KV heads of one work item (the XCD
+  // round-robin then keeps each XCD on its own heads' K/V in its L2).
+  const int u = blockIdx.x % a.Hkv;
+  const PrefillItem item = a.items[blockIdx.x / a.Hkv];
+  const int s = item.s, qt = item.qt, seq0 = item.seq0, L = item.len, p0 = item.p0;
+  const int tok_base = qt * a.bm_tok;
+  if ((s < 0) | (s >= a.n_seq) | (qt < 0) | (tok_base >= L) | (p0 < 0)) return;
+  const int n_kv = p0 + min(L, tok_base + a.bm_tok);
+
+  // ---- this lane's query row
+  const int n = lane & 31, hg = lane >> 5;
+  const int r = w * 32 + n;
+  const int hoff = r / a.bm_tok, toff = r - hoff * a.bm_tok;
+  const int qtok = tok_base + toff;
+  const bool valid = hoff < a.g && qtok < L;
+  const int qpos = valid ? p0 + qtok : 0x3fffffff;  // padding rows see every key
+  const int t_head = u * a.g + hoff;
+  int wave_min = qpos, wave_max = valid ? qpos : -1;
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    wave_min = min(wave_min, __shfl_xor(wave_min, m, 64));
+    wave_max = max(wave_max, __shfl_xor(wave_max, m, 64));
+  }
+
+  // ---- K/V sources for (sequence s, KV head u)
+  const uint16_t* kbase = (const uint16_t*)a.khat + u * a.ks_head +
+                          (a.k_packed ? (int64_t)seq0 * a.ks_tok : (int64_t)s * a.ks_seq);
+  const uint16_t* vbase = (const uint16_t*)a.v + u * a.vs_head +
+                          (a.v_packed ? (int64_t)seq0 * a.vs_tok : (int64_t)s * a.vs_seq);
+  const int64_t kstride = a.ks_tok * 2, vstride = a.vs_tok * 2;  // bytes per key row
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  // Wave w fills blocks 8w .. 8w+7 of K and of V.  Keys past n_kv (last tile
+  // only) repeat the last key: they are masked, and stay finite.
+  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    const uint32_t kdst = lds0 + stage * kStageBytes;
+    const uint32_t vdst = kdst + kKTile;
+    const char* kt = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
+    const char* vt = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
+    const int last = n_kv - 1 - t * kTileKeys;  // last valid row of the tile
+#pragma unroll
+    for (int m = 0; m < kBlocksPerWave; ++m) {
+      const int blk = wu * kBlocksPerWave + m;
+      const int row = min(blk + 32 * (lane >> 5), last);
+      load_lds16_async(kdst + blk * kKBlk, kt, (uint32_t)(row * kstride) + (lane & 31) * 16);
+      load_lds16_async(vdst + blk * kVBlk, vt, (uint32_t)(row * vstride) + (lane & 31) * 16);
+    }
+  };
+  const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
+
+  // ---- prologue: raw query row (16-byte loads), first tile, then norm + RoPE
+  u32x4 qraw[16];
+  {
+    const int64_t row = (int64_t)(seq0 + (valid ? qtok : 0)) * a.Hq + (valid ? t_head : 0);
+    const uint16_t* src = (const uint16_t*)a.q + row * a.q_row + 8 * hg;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(src + 16 * kk);
+  }
+  issue_tile(0, 0);
+  bf16x8 qf[16];
+  const int qp = valid ? qpos : 0;
+  switch (a.rot) {
+    case 32: q_prologue<32>(a, qraw, valid, qp, hg, qf); break;
+    case 64: q_prologue<64>(a, qraw, valid, qp, hg, qf); break;
+    case 128: q_prologue<128>(a, qraw, valid, qp, hg, qf); break;
+    default: q_prologue<256>(a, qraw, valid, qp, hg, qf); break;
+  }
+  const bool use_static = a.static_flag[0] != 0;
+
+  f32x16 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  // Per-lane LDS bases of the fragment reads (everything else is an immediate).
+  // K fragment (kb, kk): key 32kb + n -> block n, slot kb; dims 16kk + 8hg.
+  // V fragment (kk, db), transposed: keys 16kk + v_row0 (+8), dims 32db + v_col0 .. +3.
+  const int G = lane >> 4, lam = lane & 15;
+  const int v_row0 = 4 * (G >> 1) + (lam >> 2);
+  const int v_col0 = 16 * (G & 1) + 4 * (lam & 3);
+  const int k_base = n * kKBlk + hg * 16;
+  const int v_base = v_row0 * kVBlk + v_col0 * 2;
+
+  // One 64-key tile: S^T = K Q^T (keys 0-31, then 32-63, so the weights of the
+  // first half can form while the second half's MFMAs run), the softmax in
+  // place, O^T += V^T P^T.
+  auto tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto static_tag, auto diag_tag)
+                  __attribute__((always_inline)) {
+    constexpr bool kStatic = decltype(static_tag)::value;
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kb], 0, 0, 0);
+      }
+    }
+    // sacc[kb][j] is key key0 + 32kb + 8(j/4) + 4hg + j%4 of row n
+    if constexpr (kDiag) {
+      const int lim = qpos - key0 - 4 * hg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (32 * kb + 8 * (j >> 2) + (j & 3) > lim) sacc[kb][j] = -INFINITY;
+    }
+    float m_use = 0.f;
+    if constexpr (!kStatic) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[kb][j]);
+      mt = pair_max(mt);
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      m_use = m_new;
+    }
+    // P^T fragments: slice kk (16 keys) = registers 8(kk%2) .. +7 of block kk/2.
+    bf16x8 pf[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = sacc[kk >> 1][8 * (kk & 1) + 2 * e], x1 = sacc[kk >> 1][8 * (kk & 1) + 2 * e + 1];
+        w4[e] = kStatic ? pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1))
+                        : pack_bf16x2(__builtin_amdgcn_exp2f(x0 - m_use), __builtin_amdgcn_exp2f(x1 - m_use));
+        psum = sum_bf16x2(w4[e], psum);
+      }
+      pf[kk] = __builtin_bit_cast(bf16x8, w4);
+    }
+    l_run += psum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const lds_u8* vp = vs + v_base + 16 * (kk & 1) * kVBlk + (kk >> 1) * 512 + db * 64;
+        const bf16x8 va = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kk], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  auto run = [&](auto static_tag) __attribute__((always_inline)) {
+    for (int t = 0; t < n_tiles; ++t) {
+      // Only tile t's copies are outstanding here; once this thread's part
+      // has landed, the barrier publishes everyone's part and frees the stage
+      // of tile t-1, which receives tile t+1.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+      const int key0 = t * kTileKeys;
+      if (key0 > wave_max) continue;  // every key of the tile is in this wave's future
+      const lds_u8* ks = lds + (t & 1) * kStageBytes;
+      if (key0 + kTileKeys - 1 > wave_min)
+        tile(ks, ks + kKTile, key0, static_tag, std::true_type{});
+      else
+        tile(ks, ks + kKTile, key0, static_tag, std::false_type{});
+    }
+  };
+  if (use_static)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of row n
+  const float inv_l = 1.0f / pair_sum(l_run);
+  if (valid) {
+    const int64_t row = (int64_t)(seq0 + qtok) * a.Hq + t_head;
+    uint16_t* dst = (uint16_t*)a.out + row * kW;
+    const uint16_t* gp = a.gate ? (const uint16_t*)a.gate + row * a.q_row : nullptr;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * hg;
+        float y[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = o[db][4 * jg + c] * inv_l;
+        if (gp) {  // times sigmoid(gate) at the same dims
+          const u32x2 gr = *reinterpret_cast<const u32x2*>(gp + d);
+          const float gv[4] = {bf16_lo(gr[0]), bf16_hi(gr[0]), bf16_lo(gr[1]), bf16_hi(gr[1])};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[c] /= 1.0f + __expf(-gv[c]);
+        }
+        *reinterpret_cast<u32x2*>(dst + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_wide(const PrefillArgs& a, int n_items, hipStream_t st) {
+  if (n_items <= 0) return hipSuccess;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_prefill_wide, hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = (int64_t)n_items * a.Hkv;
+  hipLaunchKernelGGL(k_prefill_wide, dim3((unsigned)blocks), dim3(256), kSmem, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace qw

@@ -19,6 +19,7 @@ enum NormRopeMode : int {
 
 struct NormRopeArgs {
   const void* x[3];
+  int in_row[3];            // elements between consecutive head rows of x[i] (head_dim, or 2 head_dim for a gated q)
   void* out[2];             // contiguous q / k outputs (k unused when k_cache set)
   const void* gamma[2];
   int heads[3];
@@ -32,7 +33,10 @@ struct NormRopeArgs {
   int64_t n_tok;
   float eps;
   int order;                // 0: QK-Norm then RoPE; 1: RoPE then QK-Norm
-  RopeFreq rope;
+  int head_dim;             // 128 or 256
+  int rot;                  // rotated coordinates (pairs (i, i + rot/2)); head_dim for Qwen3
+  float gamma_offset;       // 0: scale = gamma; 1: zero-centred norm, scale = 1 + gamma
+  RopeFreq rope;            // theta^(-2i/rot)
 };
 
 hipError_t launch_normrope(bool bf16, const NormRopeArgs& a, hipStream_t st);
@@ -58,15 +62,19 @@ struct PlanArgs {
   const void* q_gamma;       // NULL on the fp32 path
   const void* k_gamma;
   float scale_log2e;
+  float gamma_offset;        // norm scale = gamma_offset + gamma
+  int head_dim;
   int32_t* static_flag;      // out: 1 when the static-bound softmax applies
 };
 hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
 
 struct PrefillArgs {
-  const void* q;            // raw [n_tok][Hq][128]
+  const void* q;            // raw queries; row (token n, head t) at q + (n*Hq + t)*q_row
+  int q_row;                // head_dim, or 2 head_dim when the rows carry the output gate
+  const void* gate;         // NULL, or the gate rows (q + head_dim, same strides): out *= sigmoid(gate)
   const void* q_gamma;
   const void* k_gamma;      // bf16 path: bounds the rotated-key norms
-  const void* qhat;         // fp32 path: normed+rotated q [n_tok][Hq][128] (fp32)
+  const void* qhat;         // fp32 path: normed+rotated q [n_tok][Hq][head_dim] (fp32)
   const void* khat;         // rotated keys; row (s, h, j) at khat + h*ks_head + base(s) + j*ks_tok
   int64_t ks_seq, ks_head, ks_tok;
   int k_packed;             // 1: base(s) = cu[s]*ks_tok; 0: base(s) = s*ks_seq
@@ -84,29 +92,37 @@ struct PrefillArgs {
   float scale_log2e;        // softmax scale * log2(e)
   float eps;
   int order;                // bf16 Q prologue: 0 QK-Norm then RoPE, 1 RoPE then QK-Norm
+  int head_dim;             // 128 or 256
+  int rot;                  // bf16 Q prologue: rotated coordinates
+  float gamma_offset;       // bf16 Q prologue: norm scale = gamma_offset + gamma
   RopeFreq rope;
 };
 constexpr int kPrefillRows = 256;  // query rows (g heads x bm_tok tokens) per workgroup
+constexpr int kWideRows = 128;     // the same for head_dim 256
 constexpr int kAttnF32Rows = 64;   // fp32 path: query rows per workgroup
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st);
+hipError_t launch_prefill_wide(const PrefillArgs& a, int n_items, hipStream_t st);
 hipError_t launch_attn_f32(const PrefillArgs& a, int n_items, hipStream_t st);
 
 // ---------------------------------------------------------------- decode
 struct DecodeArgs {
-  const uint16_t* qhat;     // normed+rotated new queries [n_seq][Hq][128] (bf16)
+  const uint16_t* qhat;     // normed+rotated new queries [n_seq][Hq][head_dim] (bf16)
+  const uint16_t* gate;     // NULL, or gate rows: (seq i, head t) at gate + (i*Hq + t)*q_row
+  int q_row;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   int64_t cs_seq, cs_head, cs_tok;
   const int32_t* start_pos; // keys of sequence i: slots 0 .. start_pos[i] (inclusive)
   const int32_t* chunk_off; // [n_seq + 1] prefix of chunk counts
   const int32_t* chunk_seq; // [total chunks] sequence of each chunk
-  float* partial;           // [total_chunks][Hq][kPartStride]
-  uint16_t* out;            // [n_seq][Hq][128]
+  float* partial;           // [total_chunks][Hq][head_dim + 4]: accumulators, m, l, 2 pad floats
+  uint16_t* out;            // [n_seq][Hq][head_dim]
   int n_seq, Hq, Hkv, g;
+  int head_dim;             // 128 or 256
   int chunk;                // keys per split (multiple of kDecodeKeysPerPass)
   float scale_log2e;
 };
-constexpr int kPartStride = 132;   // 128 accumulators, m, l, 2 pad floats
+inline int part_stride(int head_dim) { return head_dim + 4; }
 constexpr int kDecodeKeysPerPass = 128;  // 4 waves x 32 keys
 hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, int max_chunks, int32_t* chunk_off,
                               int32_t* chunk_seq, hipStream_t st);

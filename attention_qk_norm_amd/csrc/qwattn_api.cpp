@@ -44,6 +44,13 @@ qwattn_status hip_fail(hipError_t e, const char* what) {
   return fail(QWATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Rotated coordinates: rotary_dim, 0 meaning all of head_dim.
+int rot_dim(const qwattn_params* p) { return p->rotary_dim ? p->rotary_dim : p->head_dim; }
+
+// Elements between consecutive query head rows of q: the query and, with the
+// output gate, the gate that follows it.
+int q_row(const qwattn_params* p) { return p->output_gate ? 2 * p->head_dim : p->head_dim; }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -59,14 +66,27 @@ qwattn_status check_params(const qwattn_params* p, qwattn_dtype dt) {
   if (p->n_q_heads % p->n_kv_heads != 0)
     return fail(QWATTN_ERR_INVALID_ARG, "n_q_heads=%d is not a multiple of n_kv_heads=%d", p->n_q_heads,
                 p->n_kv_heads);
-  if (p->head_dim != QWATTN_HEAD_DIM)
-    return fail(QWATTN_ERR_UNSUPPORTED, "head_dim=%d (only 128 is supported)", p->head_dim);
+  if (p->head_dim != QWATTN_HEAD_DIM && p->head_dim != QWATTN_HEAD_DIM_GATED)
+    return fail(QWATTN_ERR_UNSUPPORTED, "head_dim=%d (128 and 256 are supported)", p->head_dim);
   if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return fail(QWATTN_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (!(p->rope_theta > 1.0) || !std::isfinite(p->rope_theta))
     return fail(QWATTN_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
   if (!(p->softmax_scale >= 0.f) || !std::isfinite(p->softmax_scale))
     return fail(QWATTN_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   if (p->order != 0 && p->order != 1) return fail(QWATTN_ERR_INVALID_ARG, "order must be 0 or 1");
+  const int rot = rot_dim(p);
+  if (rot <= 0 || rot > p->head_dim || rot % 2)
+    return fail(QWATTN_ERR_INVALID_ARG, "rotary_dim=%d must be even and in (0, head_dim]", p->rotary_dim);
+  if (!std::isfinite(p->norm_offset)) return fail(QWATTN_ERR_INVALID_ARG, "norm_offset must be finite");
+  if (p->output_gate != 0 && p->output_gate != 1) return fail(QWATTN_ERR_INVALID_ARG, "output_gate must be 0 or 1");
+  if (p->head_dim == QWATTN_HEAD_DIM) {
+    if (rot != QWATTN_HEAD_DIM || p->norm_offset != 0.f || p->output_gate)
+      return fail(QWATTN_ERR_UNSUPPORTED,
+                  "head_dim 128 takes full rotation, norm_offset 0 and no output gate (the gated-layer options "
+                  "run at head_dim 256)");
+  } else if (rot != 32 && rot != 64 && rot != 128 && rot != 256) {
+    return fail(QWATTN_ERR_UNSUPPORTED, "rotary_dim=%d at head_dim 256 (32, 64, 128 and 256 are supported)", rot);
+  }
   return QWATTN_OK;
 }
 
@@ -76,7 +96,8 @@ qwattn_status check_ptr(const void* p, const char* name, uintptr_t align = 16) {
   return QWATTN_OK;
 }
 
-qwattn_status check_cache(const qwattn_cache_desc* c, const void* kc, const void* vc, qwattn_dtype dt) {
+qwattn_status check_cache(const qwattn_cache_desc* c, const void* kc, const void* vc, qwattn_dtype dt,
+                          int head_dim) {
   qwattn_status st;
   if ((st = check_ptr(kc, "k_cache")) || (st = check_ptr(vc, "v_cache"))) return st;
   if (!c) return fail(QWATTN_ERR_INVALID_ARG, "cache descriptor is NULL");
@@ -86,19 +107,39 @@ qwattn_status check_cache(const qwattn_cache_desc* c, const void* kc, const void
   const int64_t es = elem_bytes(dt);
   if ((c->stride_seq * es) % 16 || (c->stride_head * es) % 16 || (c->stride_tok * es) % 16)
     return fail(QWATTN_ERR_INVALID_ARG, "cache strides must keep rows 16-byte aligned");
-  if (c->stride_tok < QWATTN_HEAD_DIM) return fail(QWATTN_ERR_INVALID_ARG, "cache stride_tok < head_dim");
+  if (c->stride_tok < head_dim) return fail(QWATTN_ERR_INVALID_ARG, "cache stride_tok < head_dim");
   return QWATTN_OK;
 }
 
-qw::RopeFreq rope_freq(double theta) {
-  qw::RopeFreq r;
-  for (int i = 0; i < qw::kHalf; ++i) r.w[i] = std::pow(theta, -(2.0 * i) / QWATTN_HEAD_DIM);
+// theta^(-2i/rot) for i < rot/2 (the rest zero).
+qw::RopeFreq rope_freq(const qwattn_params* p) {
+  qw::RopeFreq r{};
+  const int rot = rot_dim(p);
+  for (int i = 0; i < rot / 2; ++i) r.w[i] = std::pow(p->rope_theta, -(2.0 * i) / rot);
   return r;
 }
 
 float scale_log2e(const qwattn_params* p) {
-  const double sc = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)QWATTN_HEAD_DIM);
+  const double sc = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / std::sqrt((double)p->head_dim);
   return (float)(sc * 1.4426950408889634);
+}
+
+// Query rows per attention workgroup.
+int prefill_rows(const qwattn_params* p, qwattn_dtype dt) {
+  if (dt != QWATTN_BF16) return qw::kAttnF32Rows;
+  return p->head_dim == QWATTN_HEAD_DIM ? qw::kPrefillRows : qw::kWideRows;
+}
+
+// The norm+RoPE fields every launch shares.
+void set_norm(qw::NormRopeArgs& a, const qwattn_params* p) {
+  a.eps = p->eps;
+  a.order = p->order;
+  a.head_dim = p->head_dim;
+  a.rot = rot_dim(p);
+  a.gamma_offset = p->norm_offset;
+  a.rope = rope_freq(p);
+  a.in_row[0] = q_row(p);
+  a.in_row[1] = a.in_row[2] = p->head_dim;
 }
 
 // ------------------------------------------------------------------ prefill plan
@@ -112,15 +153,14 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
                            int64_t n_items, bool with_cache) {
   PrefillPlan pl;
   pl.g = p->n_q_heads / p->n_kv_heads;
-  const int rows = dt == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
-  pl.bm_tok = std::max(1, rows / pl.g);
+  pl.bm_tok = std::max(1, prefill_rows(p, dt) / pl.g);
   pl.max_tiles = max_tiles;
   pl.n_items = (int)n_items;
   size_t off = 0;
   pl.off_khat = off;
-  if (!with_cache) off = align256(off + (size_t)n_tok * p->n_kv_heads * QWATTN_HEAD_DIM * elem_bytes(dt));
+  if (!with_cache) off = align256(off + (size_t)n_tok * p->n_kv_heads * p->head_dim * elem_bytes(dt));
   pl.off_qhat = off;
-  if (dt == QWATTN_F32) off = align256(off + (size_t)n_tok * p->n_q_heads * QWATTN_HEAD_DIM * 4);
+  if (dt == QWATTN_F32) off = align256(off + (size_t)n_tok * p->n_q_heads * p->head_dim * 4);
   pl.off_scratch = off;
   off = align256(off + (size_t)(4 * ((int64_t)max_tiles + 1) + n_seq) * 4);
   pl.off_items = off;
@@ -151,13 +191,14 @@ DecodeLayout decode_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
   d.max_chunks = total_keys / d.chunk + n_seq;  // >= sum_i ceil(keys_i / chunk)
   size_t off = 0;
   d.off_qhat = off;
-  off = align256(off + (size_t)n_seq * p->n_q_heads * QWATTN_HEAD_DIM * elem_bytes(dt));
+  off = align256(off + (size_t)n_seq * p->n_q_heads * p->head_dim * elem_bytes(dt));
   d.off_chunk = off;
   off = align256(off + (size_t)(n_seq + 1) * 4);
   d.off_chunk_seq = off;
   off = align256(off + (size_t)d.max_chunks * 4);
   d.off_part = off;
-  if (dt == QWATTN_BF16) off = align256(off + (size_t)d.max_chunks * p->n_q_heads * qw::kPartStride * 4);
+  if (dt == QWATTN_BF16)
+    off = align256(off + (size_t)d.max_chunks * p->n_q_heads * qw::part_stride(p->head_dim) * 4);
   d.total = off;
   return d;
 }
@@ -201,6 +242,8 @@ qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtyp
   if (!k != !k_out) return fail(QWATTN_ERR_INVALID_ARG, "k and k_out must be both set or both NULL");
   if (q && ((st = check_ptr(q, "q")) || (st = check_ptr(q_out, "q_out")) || (st = check_ptr(q_gamma, "q_gamma"))))
     return st;
+  if (q && params->output_gate && q == q_out)
+    return fail(QWATTN_ERR_INVALID_ARG, "q_out may not alias q when q carries the output gate");
   if (k && ((st = check_ptr(k, "k")) || (st = check_ptr(k_out, "k_out")) || (st = check_ptr(k_gamma, "k_gamma"))))
     return st;
   if ((st = check_ptr(positions, "positions", 4))) return st;
@@ -216,9 +259,7 @@ qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtyp
   a.pos = positions;
   a.mode = qw::kPosExplicit;
   a.n_tok = n_tok;
-  a.eps = params->eps;
-  a.order = params->order;
-  a.rope = rope_freq(params->rope_theta);
+  set_norm(a, params);
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
   return QWATTN_OK;
@@ -228,8 +269,7 @@ size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype d
                                      int32_t max_seqlen, int32_t with_cache) {
   if (check_params(params, dtype) || n_seq < 0 || n_tok < 0 || max_seqlen < 0) return 0;
   const int g = params->n_q_heads / params->n_kv_heads;
-  const int rows = dtype == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
-  const int bm = std::max(1, rows / g);
+  const int bm = std::max(1, prefill_rows(params, dtype) / g);
   const int max_tiles = (max_seqlen + bm - 1) / bm;
   const int64_t n_items = n_tok / bm + n_seq;
   return prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, with_cache != 0).total;
@@ -251,10 +291,8 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   qwattn_status st;
   if ((st = check_params(params, dtype))) return st;
   const int g = params->n_q_heads / params->n_kv_heads;
-  if (dtype == QWATTN_BF16 && g > qw::kPrefillRows)
-    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d", g, qw::kPrefillRows);
-  if (dtype == QWATTN_F32 && g > qw::kAttnF32Rows)
-    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d for fp32", g, qw::kAttnF32Rows);
+  const int rows = prefill_rows(params, dtype);
+  if (g > rows) return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d", g, rows);
   if (n_seq < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_seq < 0");
   if (n_seq == 0) return QWATTN_OK;
   if (!cu_seqlens_host) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
@@ -277,7 +315,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
     if (!any_cache) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
   }
   if (any_cache) {
-    if ((st = check_cache(cache, k_cache, v_cache, dtype))) return st;
+    if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim))) return st;
     for (int s = 0; s < n_seq; ++s) {
       const int64_t p0 = append ? start_pos_host[s] : 0;
       const int64_t L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
@@ -289,7 +327,6 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   }
   if (n_tok == 0) return QWATTN_OK;
 
-  const int rows = dtype == QWATTN_BF16 ? qw::kPrefillRows : qw::kAttnF32Rows;
   const int bm = std::max(1, rows / g);
   int max_tiles = 0;
   int64_t n_items = 0;
@@ -308,8 +345,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   // ---- launches
   hipStream_t strm = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const int64_t D = QWATTN_HEAD_DIM;
-  const qw::RopeFreq rope = rope_freq(params->rope_theta);
+  const int64_t D = params->head_dim;
 
   // 1) norm + RoPE of K (and of Q for the fp32 path); K̂ -> cache or workspace, V -> cache
   qw::NormRopeArgs nr{};
@@ -329,9 +365,7 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   nr.n_seq = n_seq;
   nr.mode = qw::kPosPacked;
   nr.n_tok = n_tok;
-  nr.eps = params->eps;
-  nr.order = params->order;
-  nr.rope = rope;
+  set_norm(nr, params);
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
   if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
 
@@ -349,6 +383,8 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
     pa.q_gamma = q_gamma;
     pa.k_gamma = k_gamma;
     pa.scale_log2e = scale_log2e(params);
+    pa.gamma_offset = params->norm_offset;
+    pa.head_dim = params->head_dim;
     pa.static_flag = (int32_t*)(ws + pl.off_flag);
   }
   if ((e = qw::launch_prefill_plan(pa, strm)) != hipSuccess) return hip_fail(e, "plan launch");
@@ -356,6 +392,8 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   // 3) attention
   qw::PrefillArgs a{};
   a.q = q;
+  a.q_row = q_row(params);
+  a.gate = params->output_gate ? (const char*)q + D * elem_bytes(dtype) : nullptr;
   a.q_gamma = q_gamma;
   a.k_gamma = k_gamma;
   a.qhat = ws + pl.off_qhat;
@@ -391,10 +429,14 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.scale_log2e = scale_log2e(params);
   a.eps = params->eps;
   a.order = params->order;
-  a.rope = rope;
+  a.head_dim = params->head_dim;
+  a.rot = rot_dim(params);
+  a.gamma_offset = params->norm_offset;
+  a.rope = nr.rope;
   e = timed_launch(strm, [&] {
-    return dtype == QWATTN_BF16 ? qw::launch_prefill_bf16(a, (int)n_items, strm)
-                                : qw::launch_attn_f32(a, (int)n_items, strm);
+    if (dtype != QWATTN_BF16) return qw::launch_attn_f32(a, (int)n_items, strm);
+    return D == QWATTN_HEAD_DIM ? qw::launch_prefill_bf16(a, (int)n_items, strm)
+                                : qw::launch_prefill_wide(a, (int)n_items, strm);
   });
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return QWATTN_OK;
@@ -456,7 +498,7 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
       (st = check_ptr(start_pos, "start_pos", 4)))
     return st;
   if (!start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos_host is NULL");
-  if ((st = check_cache(cache, k_cache, v_cache, dtype))) return st;
+  if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim))) return st;
   int64_t total = 0;
   for (int i = 0; i < n_seq; ++i) {
     const int sp = start_pos_host[i];
@@ -477,7 +519,8 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
 
   hipStream_t strm = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const int64_t D = QWATTN_HEAD_DIM;
+  const int64_t D = params->head_dim;
+  const void* gate = params->output_gate ? (const char*)q + D * elem_bytes(dtype) : nullptr;
 
   // 1) prologue: q̂ -> workspace; k̂ (rotated at start_pos) and v -> cache slot start_pos
   qw::NormRopeArgs nr{};
@@ -494,15 +537,16 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
   nr.n_seq = n_seq;
   nr.mode = qw::kPosDecode;
   nr.n_tok = n_seq;
-  nr.eps = params->eps;
-  nr.order = params->order;
-  nr.rope = rope_freq(params->rope_theta);
+  set_norm(nr, params);
   hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
   if (e != hipSuccess) return hip_fail(e, "decode prologue launch");
 
   if (dtype == QWATTN_BF16) {
     qw::DecodeArgs a{};
     a.qhat = (const uint16_t*)(ws + dl.off_qhat);
+    a.gate = (const uint16_t*)gate;
+    a.q_row = q_row(params);
+    a.head_dim = params->head_dim;
     a.k_cache = (const uint16_t*)k_cache;
     a.v_cache = (const uint16_t*)v_cache;
     a.cs_seq = cache->stride_seq; a.cs_head = cache->stride_head; a.cs_tok = cache->stride_tok;
@@ -526,6 +570,9 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
   } else {
     qw::PrefillArgs a{};
     a.qhat = ws + dl.off_qhat;
+    a.gate = gate;
+    a.q_row = q_row(params);
+    a.head_dim = params->head_dim;
     a.khat = k_cache;
     a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
     a.k_packed = 0;

@@ -17,6 +17,11 @@ of a full-size case can be regenerated without drawing the rest):
     drawn per (sequence, 1024-token block); streams 6, 7: the raw K and V
     already in a decode cache, per (sequence, 1024-token block);
   * bf16 cases round every value to bf16 with round-to-nearest-even.
+Gated-layer cases (head_dim 256, the Qwen3-Next / Qwen3.5 global layers) use
+the same streams at head_dim 256, norm weights w = 0.1 N(0, 1) (the
+zero-centred norm scales by 1 + w, so the scales match the Qwen3 cases), and
+stream 8: the output-gate pre-activations, 2 N(0, 1) per (token, head, dim)
+(sigmoid then spans about 0.02 .. 0.98).
 """
 
 import math
@@ -30,7 +35,9 @@ SEED_ROOT = 0x51A7
 HEAD_DIM = 128
 BLOCK_TOKENS = 1024
 
-S_LENGTHS, S_SCALES, S_GAMMA, S_Q, S_K, S_V, S_CACHE_K, S_CACHE_V = range(8)
+S_LENGTHS, S_SCALES, S_GAMMA, S_Q, S_K, S_V, S_CACHE_K, S_CACHE_V, S_GATE = range(9)
+GATED_HEAD_DIM = 256
+GATE_SCALE = 2.0
 
 
 def round_to_bf16(x):
@@ -76,6 +83,8 @@ class CaseSpec:
     head_dim: int = HEAD_DIM
     v_scaled: bool = True      # False: v ~ N(0, 1) unscaled (q, k still scaled)
     pos_offset: int = 0
+    gated: bool = False        # gated global layer: zero-centred norm, partial RoPE, output gate
+    rot: int = HEAD_DIM        # rotated coordinates
 
     @property
     def g(self):
@@ -136,6 +145,33 @@ def custom_spec(case_id, dtype, n_q_heads, n_kv_heads, lengths, kind="prefill", 
                     lengths=[int(x) for x in lengths], v_scaled=v_scaled, eps=eps)
 
 
+# The gated global layer of Qwen3-Next-80B-A3B (2 KV heads, head_dim 256,
+# partial rotary factor 0.25; 16 query heads) at the prefill shape of the
+# Qwen3-8B workload, and a 64-sequence decode over the same context mix.
+GATED_PREFILL_CASE = 5
+GATED_DECODE_CASE = 6
+
+
+def gated_case_spec(case_id):
+    """Spec of the gated-layer workloads (prefill 5, decode 6)."""
+    if case_id == GATED_PREFILL_CASE:
+        return gated_spec(case_id, "bf16", 16, 2, [4096] * 4, rot=64,
+                          workload="qwen3-next-global-layer-prefill-bf16 B4 T4096 Hq16 Hkv2 d256 rot64")
+    if case_id == GATED_DECODE_CASE:
+        return gated_spec(case_id, "bf16", 16, 2, _lengths(case_id, ("uniform", 64, 1024, 32768)), kind="decode",
+                          rot=64, workload="qwen3-next-global-layer-decode-bf16 64seq ctx U[1024,32768] Hq16 Hkv2 d256")
+    raise ValueError(case_id)
+
+
+def gated_spec(case_id, dtype, n_q_heads, n_kv_heads, lengths, kind="prefill", theta=1e7, rot=64,
+               v_scaled=True, eps=1e-6, workload=None):
+    """Spec of a gated global-attention layer shape (head_dim 256)."""
+    return CaseSpec(case_id=case_id, workload=workload or f"gated-{case_id}", dtype=dtype,
+                    n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, theta=theta, kind=kind,
+                    lengths=[int(x) for x in lengths], v_scaled=v_scaled, eps=eps,
+                    head_dim=GATED_HEAD_DIM, gated=True, rot=rot)
+
+
 def _store(x, dtype):
     return round_to_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
@@ -153,11 +189,17 @@ def head_scales(spec):
 
 
 def gammas(spec):
-    """(gamma_q, gamma_k), each 1 + 0.1 N(0, 1) over head_dim, in the case dtype."""
+    """(gamma_q, gamma_k), each 1 + 0.1 N(0, 1) over head_dim, in the case dtype
+    (gated layers: the zero-centred weights w = 0.1 N(0, 1))."""
     rng = _rng(SEED_ROOT, spec.case_id, S_GAMMA)
-    gq = 1.0 + 0.1 * rng.standard_normal(spec.head_dim)
-    gk = 1.0 + 0.1 * rng.standard_normal(spec.head_dim)
+    base = 0.0 if spec.gated else 1.0
+    gq = base + 0.1 * rng.standard_normal(spec.head_dim)
+    gk = base + 0.1 * rng.standard_normal(spec.head_dim)
     return _store(gq.astype(np.float32), spec.dtype), _store(gk.astype(np.float32), spec.dtype)
+
+
+def _gate_scale(spec):
+    return np.full(spec.n_q_heads, GATE_SCALE, dtype=np.float32)
 
 
 def _block(spec, stream, seq, blk, n, heads, scale):
@@ -205,17 +247,27 @@ def prefill_inputs(spec):
     assert spec.kind == "prefill"
     sq, sk, sv = head_scales(spec)
     gq, gk = gammas(spec)
-    return dict(q=_packed(spec, S_Q, spec.n_q_heads, sq),
-                k=_packed(spec, S_K, spec.n_kv_heads, sk),
-                v=_packed(spec, S_V, spec.n_kv_heads, sv),
-                q_gamma=gq, k_gamma=gk, cu_seqlens=spec.cu_seqlens())
+    x = dict(q=_packed(spec, S_Q, spec.n_q_heads, sq),
+             k=_packed(spec, S_K, spec.n_kv_heads, sk),
+             v=_packed(spec, S_V, spec.n_kv_heads, sv),
+             q_gamma=gq, k_gamma=gk, cu_seqlens=spec.cu_seqlens())
+    if spec.gated:
+        x["gate"] = _packed(spec, S_GATE, spec.n_q_heads, _gate_scale(spec))
+    return x
+
+
+def q_proj_rows(q, gate):
+    """The q_proj output layout of a gated layer: per head the query, then the
+    gate ([n, H, d] twice -> [n, H, 2d])."""
+    return np.ascontiguousarray(np.concatenate([q, gate], axis=-1))
 
 
 def prefill_seq_rows(spec, seq, lo, hi, which):
     """Rows lo..hi-1 of sequence ``seq`` of 'q', 'k' or 'v' (for sampled checks)."""
     sq, sk, sv = head_scales(spec)
     stream, heads, scale = {"q": (S_Q, spec.n_q_heads, sq), "k": (S_K, spec.n_kv_heads, sk),
-                            "v": (S_V, spec.n_kv_heads, sv)}[which]
+                            "v": (S_V, spec.n_kv_heads, sv),
+                            "gate": (S_GATE, spec.n_q_heads, _gate_scale(spec))}[which]
     return seq_rows(spec, stream, seq, spec.lengths[seq], heads, scale, lo, hi)
 
 
@@ -233,8 +285,11 @@ def decode_new_token(spec):
                   for i, L in enumerate(spec.lengths)])
     v = np.stack([seq_rows(spec, S_V, i, L + 1, spec.n_kv_heads, sv, L, L + 1)[0]
                   for i, L in enumerate(spec.lengths)])
-    return dict(q=q, k=k, v=v, q_gamma=gq, k_gamma=gk,
-                start_pos=np.asarray(spec.lengths, dtype=np.int32))
+    x = dict(q=q, k=k, v=v, q_gamma=gq, k_gamma=gk, start_pos=np.asarray(spec.lengths, dtype=np.int32))
+    if spec.gated:
+        x["gate"] = np.stack([seq_rows(spec, S_GATE, i, L + 1, spec.n_q_heads, _gate_scale(spec), L, L + 1)[0]
+                              for i, L in enumerate(spec.lengths)])
+    return x
 
 
 def decode_cache_raw(spec, seq):

@@ -22,13 +22,25 @@
  *             position start_pos and never again.
  *             ["Qwen3" notes, Qwen3Attention excerpt; "第 20 章 Qwen3 与 Qwen3.5" §20.3]
  *
+ * Gated global-attention layers (Qwen3-Next, Qwen3.5; params.head_dim = 256)
+ *             ["14. Qwen 家族：从 QKV 偏置到混合注意力", section on Qwen3-Next;
+ *              "第 20 章 Qwen3 与 Qwen3.5" §20.4]:
+ *   norm      zero-centred: the scale is 1 + w (params.norm_offset = 1);
+ *   RoPE      partial: only the first rotary_dim coordinates turn, as rotate-half
+ *             pairs (i, i + rotary_dim/2) at frequencies theta^(-2i/rotary_dim);
+ *             the others pass unchanged (rotary_dim 64 of 256);
+ *   gate      q_proj gives 2 * head_dim values per query head, the query then the
+ *             gate (params.output_gate = 1); the attention output of that head is
+ *             multiplied elementwise by sigmoid(gate).
+ *
  * Conventions for every entry point
  *   - Device pointers are device memory of the current HIP device; host pointers
  *     are read during the call only.  The library allocates and frees nothing:
  *     scratch memory comes from the caller's `workspace`, sized by the
  *     *_workspace_size functions.  All device buffers stay the caller's.
- *   - Tensors are token-major and contiguous, head_dim innermost:
- *     q [n_tok][n_q_heads][128], k and v [n_tok][n_kv_heads][128].  Every tensor
+ *   - Tensors are token-major and contiguous, head_dim (d) innermost:
+ *     q [n_tok][n_q_heads][d] (or [n_tok][n_q_heads][2d] with output_gate),
+ *     k and v [n_tok][n_kv_heads][d], out [n_tok][n_q_heads][d].  Every tensor
  *     of a call has the call's dtype, gamma included; math is fp32; outputs
  *     have the input dtype.  Base pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
@@ -50,13 +62,14 @@
 extern "C" {
 #endif
 
-#define QWATTN_ABI_VERSION 2
-#define QWATTN_HEAD_DIM 128
+#define QWATTN_ABI_VERSION 3
+#define QWATTN_HEAD_DIM 128        /* Qwen3 layers                  */
+#define QWATTN_HEAD_DIM_GATED 256  /* gated Qwen3-Next / 3.5 layers */
 
 typedef enum {
   QWATTN_OK = 0,
   QWATTN_ERR_INVALID_ARG = 1,  /* bad shape, pointer, alignment or length array   */
-  QWATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim != 128, ...) */
+  QWATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim 64, ...)    */
   QWATTN_ERR_CAPACITY = 3,     /* a sequence would not fit in the cache           */
   QWATTN_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required      */
   QWATTN_ERR_HIP = 5           /* a HIP runtime call or launch failed             */
@@ -66,12 +79,19 @@ typedef enum { QWATTN_F32 = 0, QWATTN_BF16 = 1 } qwattn_dtype;
 
 typedef struct {
   int32_t n_q_heads;    /* query heads, > 0                                        */
-  int32_t n_kv_heads;   /* KV heads, > 0, divides n_q_heads; g = n_q / n_kv <= 128  */
-  int32_t head_dim;     /* must be 128                                             */
+  int32_t n_kv_heads;   /* KV heads, > 0, divides n_q_heads; g = n_q / n_kv <= 128,
+                           and <= 16 for a bf16 decode                            */
+  int32_t head_dim;     /* 128, or 256 for the gated layers                        */
   float eps;            /* RMSNorm epsilon (1e-6 for Qwen3), >= 0                  */
   double rope_theta;    /* RoPE base (1e6 dense Qwen3, 1e7 for the MoE models), > 1 */
   float softmax_scale;  /* 0 => 1/sqrt(head_dim)                                   */
   int32_t order;        /* 0 = QK-Norm then RoPE, 1 = RoPE then QK-Norm            */
+  int32_t rotary_dim;   /* leading coordinates RoPE turns; 0 => head_dim.  head_dim
+                           128: 128; head_dim 256: 32, 64, 128 or 256            */
+  float norm_offset;    /* QK-Norm scale = norm_offset + gamma: 0 (Qwen3), or 1 (the
+                           zero-centred norm); head_dim 128: 0                   */
+  int32_t output_gate;  /* 1: q holds [query | gate] per head (2 * head_dim values)
+                           and out = attention * sigmoid(gate); head_dim 128: 0  */
 } qwattn_params;
 
 /* A KV cache: element (seq s, kv head h, slot j, dim d) of k_cache / v_cache is at
@@ -86,11 +106,13 @@ typedef struct {
 } qwattn_cache_desc;
 
 /* QK-Norm then RoPE on standalone rows.
- *   q [n_tok][n_q_heads][128] and k [n_tok][n_kv_heads][128] (device): raw rows;
+ *   q [n_tok][n_q_heads][d] (with output_gate: [n_tok][n_q_heads][2d], whose gate
+ *     halves are not read) and k [n_tok][n_kv_heads][d] (device): raw rows;
  *     either may be NULL (then its output must be NULL too).
- *   q_gamma, k_gamma [128] (device): the learned scales; required with q / k.
+ *   q_gamma, k_gamma [d] (device): the learned scales; required with q / k.
  *   positions [n_tok] (device int32, >= 0): position of each token row.
- *   q_out, k_out (device): same shapes; may alias q, k (in place).
+ *   q_out [n_tok][n_q_heads][d], k_out [n_tok][n_kv_heads][d] (device); may alias
+ *     q, k (in place; not q with output_gate).
  * n_tok == 0 is a no-op.  Used on its own and to fill a cache with rotated keys. */
 qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtype,
                                   const void* q, const void* k,
@@ -99,12 +121,14 @@ qwattn_status qwattn_qk_norm_rope(const qwattn_params* params, qwattn_dtype dtyp
                                   void* q_out, void* k_out, void* stream);
 
 /* Causal GQA prefill over packed ragged sequences, with QK-Norm and RoPE fused.
- *   q [n_tok][n_q_heads][128], k, v [n_tok][n_kv_heads][128] (device): raw rows of
- *     all sequences packed one after another.
+ *   q [n_tok][n_q_heads][d] (output_gate: [n_tok][n_q_heads][2d]), k, v
+ *     [n_tok][n_kv_heads][d] (device): raw rows of all sequences packed one after
+ *     another.
  *   cu_seqlens [n_seq+1] (device int32) and cu_seqlens_host (host, same values):
  *     sequence s owns tokens cu[s] .. cu[s+1]-1 at positions 0 .. L_s-1; cu[0] = 0,
  *     non-decreasing, cu[n_seq] = n_tok.  Sequences never attend to each other.
- *   out [n_tok][n_q_heads][128] (device): attention output (before o_proj).
+ *   out [n_tok][n_q_heads][d] (device): attention output (gated, with
+ *     output_gate), before o_proj.
  *   k_cache, v_cache, cache (optional, all NULL or all set): K after norm and RoPE
  *     and V of sequence s, token j go to slot j of cache sequence s; every
  *     L_s <= capacity.
@@ -119,8 +143,8 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* One new token per sequence against a KV cache (split-K decode).
- *   q [n_seq][n_q_heads][128], k, v [n_seq][n_kv_heads][128] (device): the raw
- *     new token of each sequence.
+ *   q [n_seq][n_q_heads][d] (output_gate: [n_seq][n_q_heads][2d]), k, v
+ *     [n_seq][n_kv_heads][d] (device): the raw new token of each sequence.
  *   k_cache, v_cache, cache: slots 0 .. start_pos[i]-1 of sequence i hold K after
  *     norm and RoPE and V.  The call normalises and rotates the new k at position
  *     start_pos[i], writes it and v into slot start_pos[i] (never re-rotating the
@@ -128,7 +152,7 @@ qwattn_status qwattn_prefill(const qwattn_params* params, qwattn_dtype dtype,
  *   start_pos [n_seq] (device int32) and start_pos_host (host, same values):
  *     >= 0 and start_pos[i] + 1 <= capacity for every i, else QWATTN_ERR_CAPACITY
  *     with nothing written.
- *   out [n_seq][n_q_heads][128] (device).
+ *   out [n_seq][n_q_heads][d] (device).
  *   workspace (device, >= qwattn_decode_workspace_size bytes, 256-byte aligned).
  * n_seq == 0 is a no-op. */
 qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
@@ -145,8 +169,9 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
  * rotated at its own positions, cached K never again) and §20.9 (appending a
  * prompt in chunks gives the single-pass result; an over-long append is
  * rejected and changes nothing)].
- *   q [n_new][n_q_heads][128], k, v [n_new][n_kv_heads][128] (device): raw rows of
- *     the new tokens of all sequences, packed one sequence after another.
+ *   q [n_new][n_q_heads][d] (output_gate: [n_new][n_q_heads][2d]), k, v
+ *     [n_new][n_kv_heads][d] (device): raw rows of the new tokens of all
+ *     sequences, packed one sequence after another.
  *   cu_new [n_seq+1] (device int32) and cu_new_host (host, same values): sequence
  *     s appends tokens cu_new[s] .. cu_new[s+1]-1; cu_new[0] = 0, non-decreasing.
  *   start_pos [n_seq] (device int32) and start_pos_host (host, same values): the
@@ -157,7 +182,7 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
  *     norm and RoPE and V; the call writes the new tokens' K (normed, rotated at
  *     their positions) and V into slots start_pos[s] .. start_pos[s]+n_s-1, then
  *     new token j attends to slots 0 .. start_pos[s]+j.
- *   out [n_new][n_q_heads][128] (device).
+ *   out [n_new][n_q_heads][d] (device).
  *   workspace (device, >= qwattn_append_workspace_size bytes, 256-byte aligned).
  * With every start_pos 0 this is qwattn_prefill with a cache; one new token per
  * sequence is what qwattn_decode computes (there with a split-K kernel that

@@ -37,5 +37,6 @@ from .gated import (  # noqa: F401
     split_query_gate,
     sigmoid,
     gated_attention_prefill,
+    gated_attention_prefill_rows,
     gated_attention_append,
 )

@@ -112,6 +112,25 @@ def gated_attention_prefill(q, gate, k, v, q_w, k_w, cu_seqlens, n_q_heads, n_kv
     return out
 
 
+def gated_attention_prefill_rows(q_rows, gate_rows, k_seq, v_seq, q_w, k_w, rows, heads, n_q_heads, n_kv_heads,
+                                 eps=1e-6, theta=1e7, rot_dim=64, scale=None):
+    """Selected output rows of ONE sequence, each by the same definition as
+    :func:`gated_attention_prefill`.  ``q_rows``/``gate_rows`` hold the query
+    and gate rows of ``rows`` only (``[len(rows), Hq, d]``); ``k_seq``/``v_seq``
+    hold keys 0 .. max(rows).  Returns ``[len(rows), len(heads), d]``."""
+    q_rows, gate_rows, k_seq, v_seq = _f64(q_rows), _f64(gate_rows), _f64(k_seq), _f64(v_seq)
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = list(heads)
+    nk = int(rows.max()) + 1
+    if k_seq.shape[0] < nk or v_seq.shape[0] < nk:
+        raise ValueError("keys up to the last requested row are needed")
+    sc = _A._scale(q_rows.shape[-1], scale)
+    qh = gated_qk_norm_rope(q_rows, q_w, rows, eps, theta, rot_dim)
+    kh = gated_qk_norm_rope(k_seq[:nk], k_w, np.arange(nk), eps, theta, rot_dim)
+    out = _A._attend(qh, kh, v_seq[:nk], rows, np.arange(nk), n_q_heads, n_kv_heads, sc, heads=heads)
+    return out * sigmoid(gate_rows[:, heads, :])
+
+
 def gated_attention_append(q_new, gate_new, k_new, v_new, q_w, k_w, k_hat_cache, v_cache, start_pos,
                            n_q_heads, n_kv_heads, eps=1e-6, theta=1e7, rot_dim=64, scale=None):
     """New tokens of ONE sequence against its cache of ``start_pos`` normed and

@@ -151,7 +151,17 @@ def pin_global_layer_kv_bytes():
                                          layers=gd["global_layers"]) == gd["kv_bytes_per_token_global_layers"]
 
 
+def pin_gated_rows_api_matches_full():
+    """The sampled-row entry point equals the full prefill rows it samples."""
+    q, gate, k, v, qw, kw, cu = _case(36, [40], 8, 2)
+    o = G.gated_attention_prefill(q, gate, k, v, qw, kw, cu, 8, 2)
+    rows = np.array([0, 17, 39])
+    r = G.gated_attention_prefill_rows(q[rows], gate[rows], k, v, qw, kw, rows, [1, 6], 8, 2)
+    assert np.max(np.abs(r - o[rows][:, [1, 6]])) < 1e-13
+
+
 GATED_PINS = [
     pin_rotary_width, pin_zero_centred_norm, pin_partial_rope, pin_split_per_head, pin_gate_values,
     pin_gated_reduces_to_qwen3, pin_gated_brute_force, pin_gated_chunked_append, pin_global_layer_kv_bytes,
+    pin_gated_rows_api_matches_full,
 ]

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qwattn_abi_version() == 2
+    assert lib.qwattn_abi_version() == 3
     for st in range(6):
         assert lib.qwattn_status_str(st)
 
@@ -67,6 +67,47 @@ def test_bad_params(lib, kw, status):
     p = B.make_params(**kw)
     assert prefill(lib, p, cu(0, 5), 1) == status
     assert lib.qwattn_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=128, rotary_dim=64), B.ERR_UNSUPPORTED),       # partial rotation runs at head_dim 256
+    (dict(head_dim=128, norm_offset=1.0), B.ERR_UNSUPPORTED),
+    (dict(head_dim=128, output_gate=1), B.ERR_UNSUPPORTED),
+    (dict(head_dim=256, rotary_dim=48), B.ERR_UNSUPPORTED),       # 32, 64, 128, 256 only
+    (dict(head_dim=256, rotary_dim=258), B.ERR_INVALID_ARG),
+    (dict(head_dim=256, rotary_dim=63), B.ERR_INVALID_ARG),
+    (dict(head_dim=256, rotary_dim=-64), B.ERR_INVALID_ARG),
+    (dict(head_dim=256, output_gate=2), B.ERR_INVALID_ARG),
+    (dict(head_dim=256, norm_offset=float("nan")), B.ERR_INVALID_ARG),
+])
+def test_gated_layer_params(lib, kw, status):
+    """The gated-layer options (partial rotary, zero-centred norm, output gate)
+    are validated before anything runs."""
+    p = B.make_params(16, 2, **kw)
+    assert prefill(lib, p, cu(0, 5), 1) == status
+    assert lib.qwattn_last_error()
+
+
+def test_gated_layer_params_accepted(lib):
+    """Valid gated-layer parameters pass validation (the call then stops at a
+    later check: here the workspace size)."""
+    for rot in (0, 32, 64, 128, 256):
+        p = B.make_params(16, 2, head_dim=256, rotary_dim=rot, norm_offset=1.0, output_gate=1)
+        assert prefill(lib, p, cu(0, 5), 1, ws_bytes=16) == B.ERR_WORKSPACE
+    p = B.make_gated_params(16, 2)
+    assert (p.head_dim, p.rotary_dim, p.norm_offset, p.output_gate) == (256, 64, 1.0, 1)
+    assert B.prefill_workspace_size(p, B.BF16, 1, 5, 5, False) > 0
+    # the rotated-K buffer scales with head_dim 256; the bf16 tile is 128 rows at head_dim 256
+    a = B.prefill_workspace_size(p, B.BF16, 4, 16384, 4096, False)
+    b = B.prefill_workspace_size(p, B.BF16, 4, 16384, 4096, True)
+    assert a - b >= 16384 * 2 * 256 * 2
+    assert prefill(lib, B.make_gated_params(256, 1), cu(0, 5), 1) == B.ERR_UNSUPPORTED  # g > 128
+    # a gated query may not be normalised in place (q_out would overlap the gates)
+    f = lib.qwattn_qk_norm_rope
+    assert f(ctypes.byref(p), 1, F, None, F, None, F, 4, F, None, None) == B.ERR_INVALID_ARG
+    # the cache rows must hold head_dim 256
+    d = B.CacheDesc(2 * 100 * 128, 100 * 128, 128, 100)
+    assert prefill(lib, p, cu(0, 5), 1, cache=(F, F, d)) == B.ERR_INVALID_ARG
 
 
 def test_bad_lengths_pointers_workspace(lib):
