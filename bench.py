@@ -9,9 +9,11 @@ One step = the whole hot path on synthetic Qwen3-shaped inputs resident in HBM:
     the combine.
 Prints one JSON line.  ``value`` is prefill attention TFLOP/s (algorithmic flops:
 unmasked causal pairs only); the decode KV-read GB/s sits under ``decode``.
+Besides the step, the line carries chunked-prefill (``append``) and the gated
+head_dim-256 layer of Qwen3-Next (``gated``: prefill and decode) figures.
 
     python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--no-decode]
-                    [--no-cpu-baseline] [--gpus 1]
+                    [--no-cpu-baseline] [--no-append] [--no-gated] [--gpus 1]
 """
 
 import argparse
@@ -198,6 +200,98 @@ def measure_append(dev, n_calls=10, new_tokens=512):
                          "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
 
 
+def _timed(run, n_calls):
+    """Mean call time (torch events around the call) and mean dominant-kernel
+    time (the library's timing hook, HIP events on its stream), in ms."""
+    import torch
+    from attention_qk_norm_amd import binding as B
+    ev = HipEvents()
+    kev = [(ev.create(), ev.create()) for _ in range(n_calls)]
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for (ka, kb), (ca, cb) in zip(kev, cev):
+        B.set_timing_events(ka, kb)
+        ca.record()
+        run()
+        cb.record()
+    torch.cuda.synchronize()
+    return (float(np.mean([a.elapsed_time(b) for a, b in cev])),
+            float(np.mean([ev.elapsed_ms(a, b) for a, b in kev])))
+
+
+def measure_gated(dev, n_calls=10):
+    """The gated global layer of Qwen3-Next (head_dim 256, 16 query / 2 KV heads,
+    rotary 64 of 256, zero-centred norm, sigmoid output gate): prefill of
+    4 x 4096 tokens into a cache, and one decode step of 64 sequences with
+    contexts U[1024, 32768]."""
+    import torch
+    from attention_qk_norm_amd import accounting, binding as B, inputs
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+    res = {}
+
+    spec = inputs.gated_case_spec(inputs.GATED_PREFILL_CASE)
+    log(f"gated prefill workload: {spec.workload}")
+    x = inputs.prefill_inputs(spec)
+    p = B.make_gated_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta, rotary_dim=spec.rot)
+    q, k, v = up(inputs.q_proj_rows(x["q"], x["gate"])), up(x["k"]), up(x["v"])
+    qg, kg = up(x["q_gamma"]), up(x["k_gamma"])
+    cu, cu_h = torch.from_numpy(x["cu_seqlens"]).to(dev), x["cu_seqlens"]
+    cap = (max(spec.lengths) + 63) // 64 * 64
+    kc = torch.empty(spec.n_seq, spec.n_kv_heads, cap, 256, dtype=bf, device=dev)
+    vc = torch.empty_like(kc)
+    out = torch.empty(spec.n_tok, spec.n_q_heads, 256, dtype=bf, device=dev)
+    ws = torch.empty(B.prefill_workspace_size(p, B.BF16, spec.n_seq, spec.n_tok, max(spec.lengths), True),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: B.prefill(p, q, k, v, qg, kg, cu, cu_h, out=out, k_cache=kc, v_cache=vc, workspace=ws)
+    for _ in range(2):
+        run()
+    c_ms, k_ms = _timed(run, n_calls)
+    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads, head_dim=256)
+    res["prefill"] = {
+        "metric": "gated prefill attention TFLOP/s", "unit": "TFLOP/s", "workload": spec.workload,
+        "value": round(flops / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
+        "roofline": {"kernel": "k_prefill_wide", "bound": "mfma", "achieved": round(flops / (k_ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("k_prefill_wide", "k_prefill_wide.hip"),
+                     "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
+    del q, k, v, kc, vc, out, ws
+
+    spec = inputs.gated_case_spec(inputs.GATED_DECODE_CASE)
+    log(f"gated decode workload: {spec.workload}; building the cache")
+    x = inputs.decode_new_token(spec)
+    cap = (max(spec.lengths) + 1 + 63) // 64 * 64
+    kc = torch.zeros(spec.n_seq, spec.n_kv_heads, cap, 256, dtype=bf, device=dev)
+    vc = torch.zeros_like(kc)
+    kg = up(x["k_gamma"])
+    for b0 in range(0, spec.n_seq, 8):
+        seqs = list(range(b0, min(spec.n_seq, b0 + 8)))
+        for i, (kr, vr) in zip(seqs, inputs.decode_cache_raw_all(spec, seqs)):
+            L = spec.lengths[i]
+            _, kh = B.qk_norm_rope(p, None, up(kr), None, kg, torch.arange(L, dtype=torch.int32, device=dev))
+            kc[i, :, :L] = kh.permute(1, 0, 2)
+            vc[i, :, :L] = up(vr).permute(1, 0, 2)
+        torch.cuda.synchronize()
+    sp_h = x["start_pos"]
+    sp = torch.from_numpy(sp_h).to(dev)
+    q, k, v, qg = up(inputs.q_proj_rows(x["q"], x["gate"])), up(x["k"]), up(x["v"]), up(x["q_gamma"])
+    out = torch.empty(spec.n_seq, spec.n_q_heads, 256, dtype=bf, device=dev)
+    ws = torch.empty(B.decode_workspace_size(p, B.BF16, spec.n_seq, int(sp_h.sum())), dtype=torch.uint8, device=dev)
+    run = lambda: B.decode(p, q, k, v, qg, kg, kc, vc, sp, sp_h, out=out, workspace=ws)
+    for _ in range(2):
+        run()
+    c_ms, k_ms = _timed(run, n_calls)
+    kv = accounting.decode_kv_read_bytes(spec.lengths, spec.n_kv_heads, head_dim=256)
+    res["decode"] = {
+        "metric": "gated decode KV-read GB/s", "unit": "GB/s", "workload": spec.workload,
+        "value": round(kv / (c_ms * 1e-3) / 1e9, 1), "call_ms": round(c_ms, 4), "kv_read_bytes": kv,
+        "roofline": {"kernel": "k_decode_split", "bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kv / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_ms": round(k_ms, 4)}}
+    return res
+
+
 def cpu_baseline_prefill(spec, n_sample=3):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     the first `n_sample` whole sequences of the packed batch (all query heads,
@@ -238,6 +332,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the chunked-prefill (append) measurement")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated-layer (head_dim 256) measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -326,6 +421,11 @@ def main():
     if not args.no_append:
         log("append (chunked prefill) measurement")
         rec["append"] = measure_append(dev)
+    if not args.no_gated:
+        del pre, dec
+        torch.cuda.empty_cache()
+        log("gated-layer measurements")
+        rec["gated"] = measure_gated(dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
