@@ -1,8 +1,10 @@
 """CPU oracle for the Qwen3 attention-sublayer core: QK-Norm, rotate-half RoPE,
 causal grouped-query softmax attention (prefill over packed sequences, and
 appending new tokens against a cache of already-normed, already-rotated keys);
-and (``oracle.gated``) the gated global-attention layer of Qwen3-Next /
-Qwen3.5: zero-centred norm, partial RoPE, per-head sigmoid output gate.
+(``oracle.layer``) the sublayer around it: the bias-free q/k/v projections
+before the core and o_proj after it; and (``oracle.gated``) the gated
+global-attention layer of Qwen3-Next / Qwen3.5: zero-centred norm, partial
+RoPE, per-head sigmoid output gate.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -28,6 +30,15 @@ from .attention import (  # noqa: F401
     attention_prefill_rows,
     attention_append,
     attention_decode,
+)
+from .layer import (  # noqa: F401
+    linear,
+    split_heads,
+    merge_heads,
+    qkv_projection,
+    attention_layer_prefill,
+    attention_layer_prefill_rows,
+    attention_layer_append,
 )
 from .gated import (  # noqa: F401
     rotary_dim,

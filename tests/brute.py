@@ -96,3 +96,21 @@ def gated_prefill(q, gate, k, v, q_w, k_w, lengths, n_q_heads, n_kv_heads, eps, 
             out.append(row)
         base += L
     return out
+
+
+def linear(x, w):
+    """y[t][o] = sum_i x[t][i] * w[o][i] (bias-free linear map, W stored [out][in])."""
+    return [[sum(row[i] * w[o][i] for i in range(len(row))) for o in range(len(w))] for row in x]
+
+
+def layer_prefill(x, w_q, w_k, w_v, w_o, q_gamma, k_gamma, lengths, n_q_heads, n_kv_heads, head_dim, eps, theta):
+    """The attention sublayer: projections, head split (head h = features
+    h*d .. h*d+d-1), the core above, heads concatenated in order, o_proj."""
+    def heads(rows, n):
+        return [[[r[h * head_dim + e] for e in range(head_dim)] for h in range(n)] for r in rows]
+    q = heads(linear(x, w_q), n_q_heads)
+    k = heads(linear(x, w_k), n_kv_heads)
+    v = heads(linear(x, w_v), n_kv_heads)
+    o = prefill(q, k, v, q_gamma, k_gamma, lengths, n_q_heads, n_kv_heads, eps, theta)
+    merged = [[o[t][h][e] for h in range(n_q_heads) for e in range(head_dim)] for t in range(len(o))]
+    return linear(merged, w_o)

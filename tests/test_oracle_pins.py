@@ -191,3 +191,48 @@ def test_gated_planted_mistake_is_caught(name, monkeypatch):
         except (AssertionError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------------------ the sublayer (projections)
+
+import pins_layer  # noqa: E402
+from oracle import layer as Y  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", pins_layer.LAYER_PINS, ids=lambda f: f.__name__)
+def test_layer_pin(pin):
+    pin()
+
+
+def _linear_untransposed(x, w):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
+
+
+def _split_heads_dim_major(y, n_heads, head_dim):
+    y = np.asarray(y, dtype=np.float64)
+    return y.reshape(y.shape[0], head_dim, n_heads).transpose(0, 2, 1)
+
+
+def _merge_heads_dim_major(o):
+    o = np.asarray(o, dtype=np.float64)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1)
+
+
+LAYER_MUTATIONS = {
+    "linear_without_transpose": ("linear", _linear_untransposed),
+    "split_heads_dim_major": ("split_heads", _split_heads_dim_major),
+    "merge_heads_dim_major": ("merge_heads", _merge_heads_dim_major),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_MUTATIONS))
+def test_layer_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = LAYER_MUTATIONS[name]
+    monkeypatch.setattr(Y, attr, fn)
+    failed = []
+    for pin in pins_layer.LAYER_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
