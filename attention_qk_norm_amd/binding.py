@@ -68,6 +68,13 @@ def load(path=None):
     lib.qwattn_prefill_workspace_size.restype = sz
     lib.qwattn_decode_workspace_size.argtypes = [pp, i32, i32, i64]
     lib.qwattn_decode_workspace_size.restype = sz
+    lib.qwattn_linear.argtypes = [i32, vp, vp, i64, i32, i32, vp, vp]
+    lib.qwattn_linear.restype = i32
+    lib.qwattn_attention_layer.argtypes = [pp, i32, i32, vp, vp, vp, vp, vp, vp, ip, i32, vp, ip, vp, vp, vp, pc,
+                                           vp, sz, vp]
+    lib.qwattn_attention_layer.restype = i32
+    lib.qwattn_attention_layer_workspace_size.argtypes = [pp, i32, i32, i32, i64, i32, i32]
+    lib.qwattn_attention_layer_workspace_size.restype = sz
     lib.qwattn_status_str.argtypes = [i32]
     lib.qwattn_status_str.restype = ctypes.c_char_p
     lib.qwattn_last_error.argtypes = []
@@ -276,3 +283,61 @@ def decode(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, start
                              sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
     return out
+
+
+def linear(x, w, y=None):
+    """y = x W^T (bf16): x [m, k], w [n, k] (the weight as stored), y [m, n]."""
+    lib = load()
+    _dev(x, "x")
+    _dev(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("x and w disagree on the input width")
+    if y is None:
+        y = torch.empty(m, n, dtype=x.dtype, device=x.device)
+    _check(lib.qwattn_linear(_dtype_code(x), _ptr(x), _ptr(w), m, n, k, _ptr(y), _stream()))
+    return y
+
+
+def attention_layer_workspace_size(params, dtype_code, hidden, n_seq, n_tok, max_seqlen, with_cache):
+    return load().qwattn_attention_layer_workspace_size(ctypes.byref(params), dtype_code, hidden, n_seq, n_tok,
+                                                        max_seqlen, 1 if with_cache else 0)
+
+
+def attention_layer(params, x, w_qkv, w_o, q_gamma, k_gamma, cu_seqlens, cu_seqlens_host=None, start_pos=None,
+                    start_pos_host=None, y=None, k_cache=None, v_cache=None, workspace=None):
+    """The attention sublayer (q/k/v projections, QK-Norm, RoPE, causal GQA,
+    o_proj) over packed sequences x [n_tok, hidden]; with ``start_pos`` an
+    append against the cache.  w_qkv stacks the q, k and v projection weights
+    ([out][in] each); w_o is the o_proj weight."""
+    lib = load()
+    for t, nm in ((x, "x"), (w_qkv, "w_qkv"), (w_o, "w_o"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"),
+                  (cu_seqlens, "cu_seqlens"), (start_pos, "start_pos")):
+        _dev(t, nm)
+    cu_h = torch.as_tensor(cu_seqlens.cpu() if cu_seqlens_host is None else cu_seqlens_host,
+                           dtype=torch.int32).contiguous()
+    n_seq = cu_h.numel() - 1
+    n_tok = int(cu_h[-1]) if n_seq > 0 else 0
+    max_len = int((cu_h[1:] - cu_h[:-1]).max()) if n_seq > 0 else 0
+    sp_h = None
+    if start_pos is not None:
+        sp_h = torch.as_tensor(start_pos.cpu() if start_pos_host is None else start_pos_host,
+                               dtype=torch.int32).contiguous()
+    hidden = x.shape[1]
+    dt = _dtype_code(x)
+    if y is None:
+        y = torch.empty(n_tok, hidden, dtype=x.dtype, device=x.device)
+    desc = None
+    if k_cache is not None:
+        _check_cache_pair(params, k_cache, v_cache)
+        desc = cache_desc(k_cache)
+    nbytes = attention_layer_workspace_size(params, dt, hidden, n_seq, n_tok, max_len, k_cache is not None)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib.qwattn_attention_layer(
+        ctypes.byref(params), dt, hidden, _ptr(x), _ptr(w_qkv), _ptr(w_o), _ptr(q_gamma), _ptr(k_gamma),
+        ctypes.c_void_p(cu_seqlens.data_ptr()), cu_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq,
+        _ptr(start_pos), None if sp_h is None else sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        _ptr(y), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc) if desc else None,
+        ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
+    return y

@@ -129,4 +129,36 @@ hipError_t launch_decode_plan(const int32_t* start_pos, int n_seq, int chunk, in
 hipError_t launch_decode_split(const DecodeArgs& a, int total_chunks, hipStream_t st);
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 
+// ---------------------------------------------------------------- projections
+// y = x W^T, bf16 operands, fp32 accumulation.  x [M][K] (row stride ldx), W
+// [N][K] (row stride ldw); K a multiple of 64, N a multiple of 128.
+enum GemmEpilogue : int {
+  kGemmPlain = 0,  // y [M][N] (row stride ldy), rounded to bf16
+  kGemmQkv = 1,    // columns = Hq query, Hkv key, Hkv value head blocks of 128
+};
+struct GemmArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  int64_t M;
+  int N, K;
+  int64_t ldx, ldw;
+  uint16_t* y;              // plain
+  int64_t ldy;
+  int Hq, Hkv;              // qkv: head blocks
+  uint16_t* q_out;          // qkv: raw queries [M][Hq][128]
+  uint16_t* k_out;          // qkv: normed+rotated keys [M][Hkv][128] when k_cache is NULL
+  uint16_t* v_out;          // qkv: values [M][Hkv][128] when v_cache is NULL
+  uint16_t* k_cache;        // qkv: cache rows (seq, head, pos) as in NormRopeArgs
+  uint16_t* v_cache;
+  int64_t cs_seq, cs_head, cs_tok;
+  const int32_t* cu;        // qkv: packed sequence offsets [n_seq + 1]
+  int n_seq;
+  const int32_t* start_pos; // qkv: NULL, or (an append) each sequence's first position
+  const uint16_t* k_gamma;
+  float eps;
+  int order;
+  RopeFreq rope;
+};
+hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t st);
+
 }  // namespace qw

@@ -279,17 +279,23 @@ size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype d
 
 namespace {
 
-// Prefill, or (start_pos set) an append of new tokens at start_pos[s] .. against
-// the cache: the same three launches, with positions offset per sequence.
-qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
-                                const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
-                                const int32_t* cu_seqlens_host, int32_t n_seq, const int32_t* start_pos,
-                                const int32_t* start_pos_host, void* out, void* k_cache, void* v_cache,
-                                const qwattn_cache_desc* cache, void* workspace, size_t workspace_bytes,
-                                void* stream) {
-  const bool append = start_pos != nullptr || start_pos_host != nullptr;
+// Sizes of a prefill / append call, from the validated host lengths.
+struct SeqPlan {
+  int64_t n_tok = 0;
+  int bm = 1, max_tiles = 0;
+  int64_t n_items = 0;
+  bool append = false, any_cache = false;
+};
+
+// Checks shared by prefill, append and the sublayer: group size, lengths,
+// positions and cache capacity (nothing is enqueued on failure).  n_seq == 0
+// and n_tok == 0 return QWATTN_OK with sp.n_tok == 0.
+qwattn_status check_sequences(const qwattn_params* params, qwattn_dtype dtype, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int32_t n_seq, const int32_t* start_pos,
+                              const int32_t* start_pos_host, const void* k_cache, const void* v_cache,
+                              const qwattn_cache_desc* cache, SeqPlan& sp) {
   qwattn_status st;
-  if ((st = check_params(params, dtype))) return st;
+  sp.append = start_pos != nullptr || start_pos_host != nullptr;
   const int g = params->n_q_heads / params->n_kv_heads;
   const int rows = prefill_rows(params, dtype);
   if (g > rows) return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d", g, rows);
@@ -297,27 +303,20 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   if (n_seq == 0) return QWATTN_OK;
   if (!cu_seqlens_host) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
   if (cu_seqlens_host[0] != 0) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu_seqlens_host[0]);
-  int max_len = 0;
-  for (int s = 0; s < n_seq; ++s) {
-    const int L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
-    if (L < 0) return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d", s + 1);
-    max_len = std::max(max_len, L);
-  }
-  const int64_t n_tok = cu_seqlens_host[n_seq];
+  for (int s = 0; s < n_seq; ++s)
+    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s])
+      return fail(QWATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d", s + 1);
   if ((st = check_ptr(cu_seqlens, "cu_seqlens", 4))) return st;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
-      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")))
-    return st;
-  const bool any_cache = k_cache || v_cache || cache;
-  if (append) {
+  sp.any_cache = k_cache || v_cache || cache;
+  if (sp.append) {
     if (!start_pos || !start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos and start_pos_host are both needed");
     if ((st = check_ptr(start_pos, "start_pos", 4))) return st;
-    if (!any_cache) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
+    if (!sp.any_cache) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
   }
-  if (any_cache) {
+  if (sp.any_cache) {
     if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim))) return st;
     for (int s = 0; s < n_seq; ++s) {
-      const int64_t p0 = append ? start_pos_host[s] : 0;
+      const int64_t p0 = sp.append ? start_pos_host[s] : 0;
       const int64_t L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
       if (p0 < 0) return fail(QWATTN_ERR_INVALID_ARG, "start_pos[%d] = %lld < 0", s, (long long)p0);
       if (p0 + L > cache->capacity)
@@ -325,57 +324,59 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
                     (long long)p0, (long long)L, cache->capacity);
     }
   }
-  if (n_tok == 0) return QWATTN_OK;
-
-  const int bm = std::max(1, rows / g);
-  int max_tiles = 0;
-  int64_t n_items = 0;
+  sp.n_tok = cu_seqlens_host[n_seq];
+  sp.bm = std::max(1, rows / g);
   for (int s = 0; s < n_seq; ++s) {
-    const int nt = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + bm - 1) / bm;
-    max_tiles = std::max(max_tiles, nt);
-    n_items += nt;
+    const int nt = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + sp.bm - 1) / sp.bm;
+    sp.max_tiles = std::max(sp.max_tiles, nt);
+    sp.n_items += nt;
   }
-  if (n_items * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many tiles");
-  const PrefillPlan pl = prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, any_cache);
-  if (pl.total > 0 && (!workspace || !aligned(workspace, 256)))
+  if (sp.n_items * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many tiles");
+  return QWATTN_OK;
+}
+
+qwattn_status check_workspace(const void* workspace, size_t workspace_bytes, size_t need) {
+  if (need > 0 && (!workspace || !aligned(workspace, 256)))
     return fail(QWATTN_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < pl.total)
-    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, pl.total);
+  if (workspace_bytes < need)
+    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  return QWATTN_OK;
+}
 
-  // ---- launches
-  hipStream_t strm = (hipStream_t)stream;
-  char* ws = (char*)workspace;
+// Where the attention reads its rotated keys and values: a cache (rows by
+// sequence) or packed buffers [n_tok][Hkv][d] (rows by token).
+struct KvSource {
+  const void* khat;
+  int64_t ks_seq, ks_head, ks_tok;
+  int k_packed;
+  const void* v;
+  int64_t vs_seq, vs_head, vs_tok;
+  int v_packed;
+};
+
+KvSource cache_source(const qwattn_cache_desc* c, const void* k_cache, const void* v_cache) {
+  return {k_cache, c->stride_seq, c->stride_head, c->stride_tok, 0,
+          v_cache, c->stride_seq, c->stride_head, c->stride_tok, 0};
+}
+
+KvSource packed_source(const void* khat, const void* v, const qwattn_params* p) {
+  const int64_t D = p->head_dim;
+  return {khat, 0, D, p->n_kv_heads * D, 1, v, 0, D, p->n_kv_heads * D, 1};
+}
+
+// The tile plan and the attention kernel: q raw (bf16 path, normed and rotated
+// in the prologue) or q̂ (fp32 path, in the workspace), keys and values from kv.
+qwattn_status launch_attention(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* q_gamma,
+                               const void* k_gamma, const KvSource& kv, const int32_t* cu_seqlens,
+                               const int32_t* start_pos, int32_t n_seq, const SeqPlan& sp, const PrefillPlan& pl,
+                               char* ws, void* out, hipStream_t strm, bool timed) {
   const int64_t D = params->head_dim;
-
-  // 1) norm + RoPE of K (and of Q for the fp32 path); K̂ -> cache or workspace, V -> cache
-  qw::NormRopeArgs nr{};
-  nr.x[0] = q; nr.x[1] = k; nr.x[2] = v;
-  nr.out[0] = ws + pl.off_qhat;
-  nr.out[1] = any_cache ? nullptr : (void*)(ws + pl.off_khat);
-  nr.gamma[0] = q_gamma; nr.gamma[1] = k_gamma;
-  nr.heads[0] = dtype == QWATTN_F32 ? params->n_q_heads : 0;
-  nr.heads[1] = params->n_kv_heads;
-  nr.heads[2] = any_cache ? params->n_kv_heads : 0;
-  if (any_cache) {
-    nr.k_cache = k_cache; nr.v_cache = v_cache;
-    nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
-  }
-  nr.cu = cu_seqlens;
-  nr.pos = start_pos;  // NULL for a prefill
-  nr.n_seq = n_seq;
-  nr.mode = qw::kPosPacked;
-  nr.n_tok = n_tok;
-  set_norm(nr, params);
-  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
-  if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
-
-  // 2) tile list
   qw::PlanArgs pa{};
   pa.cu = cu_seqlens;
   pa.n_seq = n_seq;
-  pa.bm_tok = bm;
-  pa.max_tiles = max_tiles;
-  pa.n_items = (int)n_items;
+  pa.bm_tok = sp.bm;
+  pa.max_tiles = sp.max_tiles;
+  pa.n_items = (int)sp.n_items;
   pa.scratch = (int32_t*)(ws + pl.off_scratch);
   pa.start_pos = start_pos;  // NULL for a prefill
   pa.items = (qw::PrefillItem*)(ws + pl.off_items);
@@ -387,9 +388,9 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
     pa.head_dim = params->head_dim;
     pa.static_flag = (int32_t*)(ws + pl.off_flag);
   }
+  hipError_t e;
   if ((e = qw::launch_prefill_plan(pa, strm)) != hipSuccess) return hip_fail(e, "plan launch");
 
-  // 3) attention
   qw::PrefillArgs a{};
   a.q = q;
   a.q_row = q_row(params);
@@ -397,24 +398,12 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.q_gamma = q_gamma;
   a.k_gamma = k_gamma;
   a.qhat = ws + pl.off_qhat;
-  if (any_cache) {
-    a.khat = k_cache;
-    a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
-    a.k_packed = 0;
-  } else {
-    a.khat = ws + pl.off_khat;
-    a.ks_seq = 0; a.ks_head = D; a.ks_tok = params->n_kv_heads * D;
-    a.k_packed = 1;
-  }
-  if (append) {  // keys and values of the earlier tokens live only in the cache
-    a.v = v_cache;
-    a.vs_seq = cache->stride_seq; a.vs_head = cache->stride_head; a.vs_tok = cache->stride_tok;
-    a.v_packed = 0;
-  } else {
-    a.v = v;
-    a.vs_seq = 0; a.vs_head = D; a.vs_tok = params->n_kv_heads * D;
-    a.v_packed = 1;
-  }
+  a.khat = kv.khat;
+  a.ks_seq = kv.ks_seq; a.ks_head = kv.ks_head; a.ks_tok = kv.ks_tok;
+  a.k_packed = kv.k_packed;
+  a.v = kv.v;
+  a.vs_seq = kv.vs_seq; a.vs_head = kv.vs_head; a.vs_tok = kv.vs_tok;
+  a.v_packed = kv.v_packed;
   a.cu = cu_seqlens;
   a.start_pos = start_pos;  // NULL for a prefill
   a.items = pa.items;
@@ -423,8 +412,8 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.n_seq = n_seq;
   a.Hq = params->n_q_heads;
   a.Hkv = params->n_kv_heads;
-  a.g = g;
-  a.bm_tok = bm;
+  a.g = params->n_q_heads / params->n_kv_heads;
+  a.bm_tok = sp.bm;
   a.decode = 0;
   a.scale_log2e = scale_log2e(params);
   a.eps = params->eps;
@@ -432,14 +421,121 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
   a.head_dim = params->head_dim;
   a.rot = rot_dim(params);
   a.gamma_offset = params->norm_offset;
-  a.rope = nr.rope;
-  e = timed_launch(strm, [&] {
-    if (dtype != QWATTN_BF16) return qw::launch_attn_f32(a, (int)n_items, strm);
-    return D == QWATTN_HEAD_DIM ? qw::launch_prefill_bf16(a, (int)n_items, strm)
-                                : qw::launch_prefill_wide(a, (int)n_items, strm);
-  });
+  a.rope = rope_freq(params);
+  auto launch = [&] {
+    if (dtype != QWATTN_BF16) return qw::launch_attn_f32(a, (int)sp.n_items, strm);
+    return D == QWATTN_HEAD_DIM ? qw::launch_prefill_bf16(a, (int)sp.n_items, strm)
+                                : qw::launch_prefill_wide(a, (int)sp.n_items, strm);
+  };
+  e = timed ? timed_launch(strm, launch) : launch();
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return QWATTN_OK;
+}
+
+// Prefill, or (start_pos set) an append of new tokens at start_pos[s] .. against
+// the cache: the norm+RoPE pass for K (and V into the cache), then the plan and
+// the attention, with positions offset per sequence.
+qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                                const void* v, const void* q_gamma, const void* k_gamma, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t n_seq, const int32_t* start_pos,
+                                const int32_t* start_pos_host, void* out, void* k_cache, void* v_cache,
+                                const qwattn_cache_desc* cache, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  qwattn_status st;
+  if ((st = check_params(params, dtype))) return st;
+  SeqPlan sp;
+  if ((st = check_sequences(params, dtype, cu_seqlens, cu_seqlens_host, n_seq, start_pos, start_pos_host, k_cache,
+                            v_cache, cache, sp)))
+    return st;
+  if (n_seq == 0) return QWATTN_OK;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")))
+    return st;
+  if (sp.n_tok == 0) return QWATTN_OK;
+  const PrefillPlan pl = prefill_layout(params, dtype, n_seq, sp.n_tok, sp.max_tiles, sp.n_items, sp.any_cache);
+  if ((st = check_workspace(workspace, workspace_bytes, pl.total))) return st;
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  // 1) norm + RoPE of K (and of Q for the fp32 path); K̂ -> cache or workspace, V -> cache
+  qw::NormRopeArgs nr{};
+  nr.x[0] = q; nr.x[1] = k; nr.x[2] = v;
+  nr.out[0] = ws + pl.off_qhat;
+  nr.out[1] = sp.any_cache ? nullptr : (void*)(ws + pl.off_khat);
+  nr.gamma[0] = q_gamma; nr.gamma[1] = k_gamma;
+  nr.heads[0] = dtype == QWATTN_F32 ? params->n_q_heads : 0;
+  nr.heads[1] = params->n_kv_heads;
+  nr.heads[2] = sp.any_cache ? params->n_kv_heads : 0;
+  if (sp.any_cache) {
+    nr.k_cache = k_cache; nr.v_cache = v_cache;
+    nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
+  }
+  nr.cu = cu_seqlens;
+  nr.pos = start_pos;  // NULL for a prefill
+  nr.n_seq = n_seq;
+  nr.mode = qw::kPosPacked;
+  nr.n_tok = sp.n_tok;
+  set_norm(nr, params);
+  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
+  if (e != hipSuccess) return hip_fail(e, "norm+RoPE launch");
+
+  // 2) plan + attention.  K̂ from the cache or the workspace; V from the cache
+  // for an append (the earlier tokens' values live only there), else the input.
+  KvSource kv = sp.any_cache ? cache_source(cache, k_cache, v_cache) : packed_source(ws + pl.off_khat, v, params);
+  if (!sp.append) {
+    const KvSource pv = packed_source(nullptr, v, params);
+    kv.v = v; kv.vs_seq = pv.vs_seq; kv.vs_head = pv.vs_head; kv.vs_tok = pv.vs_tok; kv.v_packed = 1;
+  }
+  return launch_attention(params, dtype, q, q_gamma, k_gamma, kv, cu_seqlens, start_pos, n_seq, sp, pl, ws, out,
+                          strm, true);
+}
+
+// Workspace of the sublayer: the prefill plan (and K̂ without a cache), then
+// raw q and the attention output (bf16, [n_tok][Hq][128]), and V without a cache.
+struct LayerPlan {
+  PrefillPlan pl;
+  size_t off_q = 0, off_o = 0, off_v = 0, total = 0;
+};
+
+LayerPlan layer_layout(const qwattn_params* p, int n_seq, int64_t n_tok, int max_tiles, int64_t n_items,
+                       bool with_cache) {
+  LayerPlan lp;
+  lp.pl = prefill_layout(p, QWATTN_BF16, n_seq, n_tok, max_tiles, n_items, with_cache);
+  size_t off = lp.pl.total;
+  const size_t qbytes = (size_t)n_tok * p->n_q_heads * p->head_dim * 2;
+  lp.off_q = off;
+  off = align256(off + qbytes);
+  lp.off_o = off;
+  off = align256(off + qbytes);
+  lp.off_v = off;
+  if (!with_cache) off = align256(off + (size_t)n_tok * p->n_kv_heads * p->head_dim * 2);
+  lp.total = off;
+  return lp;
+}
+
+qwattn_status check_layer_params(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden) {
+  qwattn_status st;
+  if ((st = check_params(params, dtype))) return st;
+  if (dtype != QWATTN_BF16) return fail(QWATTN_ERR_UNSUPPORTED, "the sublayer runs in bf16");
+  if (params->head_dim != QWATTN_HEAD_DIM)
+    return fail(QWATTN_ERR_UNSUPPORTED, "the sublayer runs at head_dim 128 (the Qwen3 layers)");
+  if (hidden <= 0 || hidden % 128)
+    return fail(hidden <= 0 ? QWATTN_ERR_INVALID_ARG : QWATTN_ERR_UNSUPPORTED,
+                "hidden=%d must be a positive multiple of 128", hidden);
+  return QWATTN_OK;
+}
+
+// y = x W^T launch (plain epilogue).
+hipError_t launch_linear(const void* x, const void* w, int64_t m, int n, int k, void* y, hipStream_t strm) {
+  qw::GemmArgs g{};
+  g.x = (const uint16_t*)x;
+  g.w = (const uint16_t*)w;
+  g.M = m; g.N = n; g.K = k;
+  g.ldx = k; g.ldw = k;
+  g.y = (uint16_t*)y;
+  g.ldy = n;
+  return qw::launch_gemm(g, qw::kGemmPlain, strm);
 }
 
 }  // namespace
@@ -592,6 +688,97 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
     if ((e = timed_launch(strm, [&] { return qw::launch_attn_f32(a, n_seq, strm); })) != hipSuccess)
       return hip_fail(e, "decode attention launch");
   }
+  return QWATTN_OK;
+}
+
+qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, int64_t m, int32_t n, int32_t k,
+                            void* y, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if (dtype != QWATTN_BF16) return fail(QWATTN_ERR_UNSUPPORTED, "qwattn_linear runs in bf16");
+  if (m < 0 || n <= 0 || k <= 0) return fail(QWATTN_ERR_INVALID_ARG, "m >= 0, n > 0 and k > 0 are required");
+  if (n % 128 || k % 64)
+    return fail(QWATTN_ERR_UNSUPPORTED, "n=%d must be a multiple of 128 and k=%d of 64", n, k);
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(w, "w")) || (st = check_ptr(y, "y"))) return st;
+  if (m == 0) return QWATTN_OK;
+  hipStream_t strm = (hipStream_t)stream;
+  const hipError_t e = timed_launch(strm, [&] { return launch_linear(x, w, m, n, k, y, strm); });
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return QWATTN_OK;
+}
+
+size_t qwattn_attention_layer_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden,
+                                             int32_t n_seq, int64_t n_tok, int32_t max_seqlen, int32_t with_cache) {
+  if (check_layer_params(params, dtype, hidden) || n_seq < 0 || n_tok < 0 || max_seqlen < 0) return 0;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  const int bm = std::max(1, prefill_rows(params, dtype) / g);
+  const int max_tiles = (max_seqlen + bm - 1) / bm;
+  return layer_layout(params, n_seq, n_tok, max_tiles, n_tok / bm + n_seq, with_cache != 0).total;
+}
+
+qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden, const void* x,
+                                     const void* w_qkv, const void* w_o, const void* q_gamma, const void* k_gamma,
+                                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t n_seq,
+                                     const int32_t* start_pos, const int32_t* start_pos_host, void* y, void* k_cache,
+                                     void* v_cache, const qwattn_cache_desc* cache, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if ((st = check_layer_params(params, dtype, hidden))) return st;
+  SeqPlan sp;
+  if ((st = check_sequences(params, dtype, cu_seqlens, cu_seqlens_host, n_seq, start_pos, start_pos_host, k_cache,
+                            v_cache, cache, sp)))
+    return st;
+  if (n_seq == 0) return QWATTN_OK;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(w_qkv, "w_qkv")) || (st = check_ptr(w_o, "w_o")) ||
+      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(y, "y")))
+    return st;
+  if (sp.n_tok == 0) return QWATTN_OK;
+  const LayerPlan lp = layer_layout(params, n_seq, sp.n_tok, sp.max_tiles, sp.n_items, sp.any_cache);
+  if ((st = check_workspace(workspace, workspace_bytes, lp.total))) return st;
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int D = params->head_dim, Hq = params->n_q_heads, Hkv = params->n_kv_heads;
+
+  // 1) x W_qkv^T: raw q -> workspace; K̂ (normed, rotated at each token's
+  // position) and V -> the cache, or packed workspace buffers
+  qw::GemmArgs g{};
+  g.x = (const uint16_t*)x;
+  g.w = (const uint16_t*)w_qkv;
+  g.M = sp.n_tok;
+  g.N = (Hq + 2 * Hkv) * D;
+  g.K = hidden;
+  g.ldx = hidden; g.ldw = hidden;
+  g.Hq = Hq; g.Hkv = Hkv;
+  g.q_out = (uint16_t*)(ws + lp.off_q);
+  if (sp.any_cache) {
+    g.k_cache = (uint16_t*)k_cache; g.v_cache = (uint16_t*)v_cache;
+    g.cs_seq = cache->stride_seq; g.cs_head = cache->stride_head; g.cs_tok = cache->stride_tok;
+  } else {
+    g.k_out = (uint16_t*)(ws + lp.pl.off_khat);
+    g.v_out = (uint16_t*)(ws + lp.off_v);
+  }
+  g.cu = cu_seqlens;
+  g.n_seq = n_seq;
+  g.start_pos = start_pos;  // NULL for a prefill
+  g.k_gamma = (const uint16_t*)k_gamma;
+  g.eps = params->eps;
+  g.order = params->order;
+  g.rope = rope_freq(params);
+  hipError_t e = timed_launch(strm, [&] { return qw::launch_gemm(g, qw::kGemmQkv, strm); });
+  if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
+
+  // 2) plan + attention -> O [n_tok][Hq][128] in the workspace
+  const KvSource kv = sp.any_cache ? cache_source(cache, k_cache, v_cache)
+                                   : packed_source(ws + lp.pl.off_khat, ws + lp.off_v, params);
+  if ((st = launch_attention(params, dtype, ws + lp.off_q, q_gamma, k_gamma, kv, cu_seqlens, start_pos, n_seq, sp,
+                             lp.pl, ws, ws + lp.off_o, strm, false)))
+    return st;
+
+  // 3) o_proj: y = O W_o^T (O's heads concatenated in order)
+  if ((e = launch_linear(ws + lp.off_o, w_o, sp.n_tok, hidden, Hq * D, y, strm)) != hipSuccess)
+    return hip_fail(e, "o_proj launch");
   return QWATTN_OK;
 }
 

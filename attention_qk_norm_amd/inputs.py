@@ -22,6 +22,10 @@ the same streams at head_dim 256, norm weights w = 0.1 N(0, 1) (the
 zero-centred norm scales by 1 + w, so the scales match the Qwen3 cases), and
 stream 8: the output-gate pre-activations, 2 N(0, 1) per (token, head, dim)
 (sigmoid then spans about 0.02 .. 0.98).
+Sublayer cases (projections around the core): stream 9, the layer input rows
+x ~ N(0, 1) per (sequence, 1024-token block); streams 10 and 11, the stacked
+q/k/v weight and the o_proj weight, N(0, 1) / sqrt(fan-in) per 1024-row block
+(so q, k, v and y come out with unit scale).
 """
 
 import math
@@ -35,7 +39,7 @@ SEED_ROOT = 0x51A7
 HEAD_DIM = 128
 BLOCK_TOKENS = 1024
 
-S_LENGTHS, S_SCALES, S_GAMMA, S_Q, S_K, S_V, S_CACHE_K, S_CACHE_V, S_GATE = range(9)
+S_LENGTHS, S_SCALES, S_GAMMA, S_Q, S_K, S_V, S_CACHE_K, S_CACHE_V, S_GATE, S_X, S_WQKV, S_WO = range(12)
 GATED_HEAD_DIM = 256
 GATE_SCALE = 2.0
 
@@ -161,6 +165,66 @@ def gated_case_spec(case_id):
         return gated_spec(case_id, "bf16", 16, 2, _lengths(case_id, ("uniform", 64, 1024, 32768)), kind="decode",
                           rot=64, workload="qwen3-next-global-layer-decode-bf16 64seq ctx U[1024,32768] Hq16 Hkv2 d256")
     raise ValueError(case_id)
+
+
+# The attention sublayer of Qwen3-8B (hidden 4096, 32 / 8 heads) at the
+# 4 x 4096 prefill shape.
+LAYER_CASE = 7
+LAYER_HIDDEN = {LAYER_CASE: 4096}
+
+
+def layer_case_spec():
+    spec = case_spec(1)
+    spec.case_id = LAYER_CASE
+    spec.workload = "qwen3-8b-attention-sublayer-bf16 B4 T4096 hidden4096 Hq32 Hkv8"
+    return spec
+
+
+def _weight(spec, stream, rows, cols):
+    out = np.empty((rows, cols), dtype=np.float32)
+
+    def run(b):
+        r1 = min(rows, b + BLOCK_TOKENS)
+        w = _rng(SEED_ROOT, spec.case_id, stream, b // BLOCK_TOKENS).standard_normal((r1 - b, cols), dtype=np.float32)
+        out[b:r1] = _store(w * np.float32(1.0 / math.sqrt(cols)), spec.dtype)
+
+    list(_pool().map(run, range(0, rows, BLOCK_TOKENS)))
+    return out
+
+
+def layer_weights(spec, hidden):
+    """(w_qkv [(Hq + 2 Hkv) d, hidden], w_o [hidden, Hq d]): the stacked q/k/v
+    projection weights and the o_proj weight, each stored [out][in]."""
+    d = spec.head_dim
+    return (_weight(spec, S_WQKV, (spec.n_q_heads + 2 * spec.n_kv_heads) * d, hidden),
+            _weight(spec, S_WO, hidden, spec.n_q_heads * d))
+
+
+def layer_x(spec, hidden, seq=None, lo=0, hi=None):
+    """Layer input rows: all sequences packed [n_tok, hidden], or rows lo..hi-1
+    of sequence ``seq``."""
+    def rows(s, a, b):
+        L = spec.lengths[s]
+        out = np.empty((b - a, hidden), dtype=np.float32)
+        for blk in range(a // BLOCK_TOKENS, (b - 1) // BLOCK_TOKENS + 1 if b > a else 0):
+            s0 = blk * BLOCK_TOKENS
+            n = min(BLOCK_TOKENS, L - s0)
+            x = _store(_rng(SEED_ROOT, spec.case_id, S_X, s, blk).standard_normal((n, hidden), dtype=np.float32),
+                       spec.dtype)
+            c0, c1 = max(a, s0), min(b, s0 + n)
+            out[c0 - a:c1 - a] = x[c0 - s0:c1 - s0]
+        return out
+
+    if seq is not None:
+        return rows(seq, lo, spec.lengths[seq] if hi is None else hi)
+    cu = spec.cu_seqlens()
+    out = np.empty((int(cu[-1]), hidden), dtype=np.float32)
+
+    def run(s):
+        out[cu[s]:cu[s + 1]] = rows(s, 0, spec.lengths[s])
+
+    list(_pool().map(run, range(spec.n_seq)))
+    return out
 
 
 def gated_spec(case_id, dtype, n_q_heads, n_kv_heads, lengths, kind="prefill", theta=1e7, rot=64,

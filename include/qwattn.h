@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QWATTN_ABI_VERSION 3
+#define QWATTN_ABI_VERSION 4
 #define QWATTN_HEAD_DIM 128        /* Qwen3 layers                  */
 #define QWATTN_HEAD_DIM_GATED 256  /* gated Qwen3-Next / 3.5 layers */
 
@@ -196,6 +196,53 @@ qwattn_status qwattn_append(const qwattn_params* params, qwattn_dtype dtype,
                             int32_t n_seq, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* y = x W^T, the bias-free linear map of the sublayer's projections
+ * ["Qwen3" notes, Qwen3Attention excerpt: q_proj, k_proj, v_proj, o_proj are
+ * nn.Linear without bias; "7.2 Qwen3 全规模实现" §7.2.1 listing].
+ *   x [m][k], w [n][k] (the weight as stored, out x in), y [m][n] (device, bf16,
+ *   row-major, 16-byte aligned).  fp32 accumulation, y rounded to bf16.
+ *   n a multiple of 128 and k a multiple of 64 (QWATTN_ERR_UNSUPPORTED else);
+ *   m == 0 is a no-op.  Only QWATTN_BF16. */
+qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, int64_t m, int32_t n, int32_t k,
+                            void* y, void* stream);
+
+/* The whole attention sublayer of a Qwen3 layer over packed sequences (prefill),
+ * or an append against the cache: q/k/v projections, QK-Norm, RoPE, causal GQA
+ * attention, o_proj ["Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE
+ * -> attention -> o_proj; "7.2 Qwen3 全规模实现" §7.2.1 listing: heads
+ * concatenated in order before out_proj].
+ *   hidden: model width (a multiple of 128); x [n_tok][hidden] (device): the
+ *     layer input rows, packed as for qwattn_prefill.
+ *   w_qkv [(n_q_heads + 2 n_kv_heads) * 128][hidden] (device): the q_proj, k_proj
+ *     and v_proj weights (each stored [out][in]) stacked in that order; head h of
+ *     a projection owns its output features h*128 .. h*128+127.
+ *   w_o [hidden][n_q_heads * 128] (device): the o_proj weight.
+ *   q_gamma, k_gamma [128] (device).
+ *   cu_seqlens / cu_seqlens_host, n_seq: as for qwattn_prefill.
+ *   start_pos, start_pos_host: NULL for a prefill (positions 0 ..), or both set
+ *     for an append (as for qwattn_append; the cache is then required).
+ *   y [n_tok][hidden] (device): the sublayer output (before the residual add).
+ *   k_cache, v_cache, cache: optional for a prefill, required for an append;
+ *     the fused projection writes K after norm and RoPE and V straight into the
+ *     slots of each token.
+ *   workspace (device, >= qwattn_attention_layer_workspace_size, 256-byte
+ *     aligned).
+ * Only QWATTN_BF16 and head_dim 128 (QWATTN_ERR_UNSUPPORTED else); fp32
+ * accumulation in every product; q, k, v, the attention output and y are each
+ * rounded to bf16 once.  n_seq == 0 or n_tok == 0 is a no-op. */
+qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden,
+                                     const void* x, const void* w_qkv, const void* w_o,
+                                     const void* q_gamma, const void* k_gamma,
+                                     const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t n_seq,
+                                     const int32_t* start_pos, const int32_t* start_pos_host,
+                                     void* y, void* k_cache, void* v_cache, const qwattn_cache_desc* cache,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qwattn_attention_layer needs (0 on invalid params). */
+size_t qwattn_attention_layer_workspace_size(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden,
+                                             int32_t n_seq, int64_t n_tok, int32_t max_seqlen,
+                                             int32_t with_cache);
+
 /* Workspace bytes qwattn_append needs: n_new new tokens in all, at most max_new
  * in one sequence (0 on invalid params). */
 size_t qwattn_append_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
@@ -214,10 +261,11 @@ size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dt
 
 /* Timing hook for benchmarks and profilers.  `begin` and `end` are hipEvent_t
  * handles (or both NULL to clear).  The calling thread's next qwattn_prefill,
- * qwattn_append or qwattn_decode records `begin` on its stream right before its
- * dominant kernel (the attention kernel of prefill and append, the split kernel
- * of decode) and `end` right after it, then clears the hook.  Setting it
- * enqueues nothing. */
+ * qwattn_append, qwattn_decode, qwattn_linear or qwattn_attention_layer records
+ * `begin` on its stream right before its dominant kernel (the attention kernel
+ * of prefill and append, the split kernel of decode, the GEMM of linear, the
+ * fused q/k/v projection of the sublayer) and `end` right after it, then clears
+ * the hook.  Setting it enqueues nothing. */
 qwattn_status qwattn_set_timing_events(void* begin, void* end);
 
 const char* qwattn_status_str(qwattn_status status); /* static string             */

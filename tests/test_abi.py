@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qwattn_abi_version() == 3
+    assert lib.qwattn_abi_version() == 4
     for st in range(6):
         assert lib.qwattn_status_str(st)
 
