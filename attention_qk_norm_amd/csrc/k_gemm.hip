@@ -27,6 +27,8 @@
 // directly (global_load_lds_dwordx4) into a two-stage ring of padded 1 KB
 // blocks (row r in block r % 32, slot r / 32; 16-byte skew between blocks, so
 // the 16 rows of a fragment read land in 16 distinct bank groups).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace qw {
@@ -37,6 +39,7 @@ constexpr int kBlk = 1040;                 // 1 KB block (8 rows x 128 B) + 16 B
 constexpr int kTile = 32 * kBlk;           // one 256 x 64 operand tile
 constexpr int kStageBytes = 2 * kTile;     // x tile, then W tile
 constexpr int kSmem = 2 * kStageBytes;     // two stages
+constexpr int kThreads = 512;              // 8 waves: two per SIMD
 // qkv: after the ring, the key norm scale (128 floats) and the RoPE
 // frequencies (64 doubles), read per lane in the epilogue.
 constexpr int kGammaOff = kSmem, kFreqOff = kSmem + 512, kSmemQkv = kSmem + 1024;
@@ -44,17 +47,6 @@ static_assert(kSmemQkv <= 160 * 1024, "LDS per workgroup");
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
-}
-
-// Direct HBM -> LDS copy of 16 bytes per lane (lane l's bytes land at
-// lds_base + 16 l; M0 holds the wave-uniform base, one wait state after
-// writing it).  Inline assembly, so the compiler does not wait for every
-// outstanding copy before each LDS read: the K loop waits for its own copies.
-__device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_base), "v"(voff), "s"(gbase)
-               : "memory", "m0");
 }
 
 // Sequence and position of packed token n: last s with cu[s] <= n.
@@ -69,18 +61,32 @@ __device__ __forceinline__ void token_position(const GemmArgs& a, int64_t n, int
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   lds_u8* lds = (lds_u8*)(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wt = w >> 1, wc = w & 1;
+  const int wt = w >> 1, wc = w & 1;  // token quarter (64 tokens), column half (128 columns)
   const int n = lane & 31, hg = lane >> 5;
 
-  // Consecutive workgroups take consecutive column tiles of one token tile;
-  // the 8 XCDs receive workgroups round-robin, so each XCD keeps a fixed
-  // subset of the weight column tiles in its L2 while the token tiles stream.
+  // Tile order, XCD-aware.  Workgroups are dealt round-robin to the 8 XCDs
+  // (blockIdx b runs on XCD b % 8), each with its own L2.  When the tile grid
+  // splits evenly, XCD x takes one region of a 4 x 2 grid of regions (a
+  // quarter of the token tiles, half of the column tiles) and walks it row by
+  // row, so an XCD streams only its own quarter of x and half of W; every
+  // weight panel is then reused by the XCD's concurrent token tiles from its
+  // L2.  Otherwise: consecutive workgroups take consecutive column tiles.
   const int tiles_n = (a.N + kBN - 1) / kBN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int tiles_m = (int)((a.M + kBM - 1) / kBM);
+  int tm, tn;
+  if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
+    const int x = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int rn = tiles_n / 2;
+    tm = (x >> 1) * (tiles_m / 4) + idx / rn;
+    tn = (x & 1) * rn + idx % rn;
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x - tm * tiles_n;
+  }
   const int64_t row0 = (int64_t)tm * kBM;
   const int col0 = tn * kBN;
 
@@ -89,75 +95,109 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
   const int64_t xrow = a.ldx * 2, wrow = a.ldw * 2;  // bytes per row
   const int last_x = (int)min((int64_t)kBM - 1, a.M - 1 - row0);
   const int last_w = min(kBN - 1, a.N - 1 - col0);
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  // Wave w fills blocks 8w .. 8w+7 of both tiles; rows past the matrix repeat
-  // its last row (their results are never stored).
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    const uint32_t xdst = lds0 + stage * kStageBytes, wdst = xdst + kTile;
-    const char* xk = xbase + (int64_t)kt * kBK * 2;
-    const char* wk = wbase + (int64_t)kt * kBK * 2;
+  // Staging: wave w moves blocks 4w .. 4w+3 of both tiles; lane l carries
+  // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- so its LDS
+  // address inside a block is 16 l.  Rows past the matrix repeat its last row
+  // (their results are never stored).
+  uint32_t xo[4], wo[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int blk = wu * 8 + m;
-      const int r = blk + 32 * (lane >> 3);
-      load_lds16_async(xdst + blk * kBlk, xk, (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16);
-      load_lds16_async(wdst + blk * kBlk, wk, (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16);
-    }
+  for (int m = 0; m < 4; ++m) {
+    const int r = w * 4 + m + 32 * (lane >> 3);
+    xo[m] = (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16;
+    wo[m] = (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16;
+  }
+  u32x4 stg[8];  // one K step in flight: x blocks (0..3), then W blocks (4..7)
+  auto gload = [&](int kt, int m) __attribute__((always_inline)) {
+    const char* p = (m < 4 ? xbase + xo[m] : wbase + wo[m - 4]) + (int64_t)kt * kBK * 2;
+    stg[m] = *reinterpret_cast<const u32x4*>(p);
+  };
+  auto lwrite = [&](int kt, int m) __attribute__((always_inline)) {
+    lds_u8* base = lds + (kt & 1) * kStageBytes + (m < 4 ? 0 : kTile) + (w * 4 + (m & 3)) * kBlk + lane * 16;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base) = stg[m];
   };
 
-  f32x16 acc[4][4];  // [column block jc][token block it]
+  f32x16 acc[4][2];  // [column block jc][token block it]
 #pragma unroll
   for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[jc][it][j] = 0.f;
 
-  // Fragment (row block b of the wave's half, k16 step s): row 32b + n of the
-  // half -> block n, slot 4 half + b; 16-byte chunk 2s + hg.
-  const int xoff = n * kBlk + hg * 16 + wt * 512;
+  // Fragment (k16 step s): tile row r -> block r % 32, slot r / 32; 16-byte
+  // chunk 2s + hg.  Token block it of the wave: row 64 wt + 32 it + n (slot
+  // 2 wt + it); column block jc: row 128 wc + 32 jc + n (slot 4 wc + jc).
+  const int xoff = n * kBlk + hg * 16 + wt * 256;
   const int woff = n * kBlk + hg * 16 + wc * 512;
   const int nk = a.K / kBK;
-  issue(0, 0);
   float* gk_lds = (float*)(smem + kGammaOff);
   double* w_lds = (double*)(smem + kFreqOff);
-  if constexpr (EPI == kGemmQkv) {  // published by the loop's first barrier
+  if constexpr (EPI == kGemmQkv) {  // published by the first barrier below
     if (tid < 128) gk_lds[tid] = bf16_to_f32(a.k_gamma[tid]);
     else if (tid < 192) w_lds[tid - 128] = a.rope.w[tid - 128];
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    // Only step kt's copies are outstanding here; once this thread's part has
-    // landed, the barrier publishes everyone's part and frees the other stage.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+  // K step 0 into LDS stage 0; K step 1 into the staging registers.
+#pragma unroll
+  for (int m = 0; m < 8; ++m) gload(0, m);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) lwrite(0, m);
+  if (nk > 1)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) gload(1, m);
+  bf16x8 wf[2][4], xf[2][2];
+  auto read = [&](int kt, int s, int r) __attribute__((always_inline)) {
+    // order: W 0, x 0, x 1, W 1..3 -- the first MFMAs of a step need W 0 and x 0, 1
     const lds_u8* xs = lds + (kt & 1) * kStageBytes;
     const lds_u8* ws = xs + kTile;
+    const int buf = s & 1;
+    if (r == 0) wf[buf][0] = lds_load_b128(ws + woff + s * 32);
+    else if (r < 3) xf[buf][r - 1] = lds_load_b128(xs + xoff + (r - 1) * 128 + s * 32);
+    else wf[buf][r - 2] = lds_load_b128(ws + woff + (r - 2) * 128 + s * 32);
+  };
+  // One K step: kMore / kMore2 say whether K steps kt+1 / kt+2 exist
+  // (compile-time in the steady state, so the MFMA stream has no branches).
+  auto step = [&](int kt, auto more_tag, auto more2_tag) __attribute__((always_inline)) {
+    constexpr bool kMore = decltype(more_tag)::value, kMore2 = decltype(more2_tag)::value;
+    // Step kt is in LDS (every wave's writes done and published); the other
+    // stage, which held step kt-1, is free for step kt+1.
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 6; ++r) read(kt, 0, r);
+    // Four k16 steps of 8 MFMAs.  The 6 fragments of step s+1 are read during
+    // step s; after every fourth MFMA one staged block of K step kt+1 goes to
+    // LDS and its register is refilled with the same block of K step kt+2, so
+    // each load has a whole K step to land.  sched_barrier keeps that order;
+    // the two waves of a SIMD interleave their streams.
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      bf16x8 wf[4], xf[4];
+      const int buf = s & 1;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        wf[b] = lds_load_b128(ws + woff + b * 128 + s * 32);
-        xf[b] = lds_load_b128(xs + xoff + b * 128 + s * 32);
+      for (int i = 0; i < 8; ++i) {
+        const int jc = i >> 1, it = i & 1;
+        acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][jc], xf[buf][it], acc[jc][it], 0, 0, 0);
+        if (s + 1 < kBK / 16 && i < 6) read(kt, s + 1, i);
+        if ((i & 3) == 3) {
+          const int m = 2 * s + (i >> 2);
+          if constexpr (kMore) lwrite(kt + 1, m);
+          if constexpr (kMore2) gload(kt + 2, m);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int jc = 0; jc < 4; ++jc)
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-          acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[jc], xf[it], acc[jc][it], 0, 0, 0);
     }
-  }
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
+  if (kt + 1 < nk) step(kt++, std::true_type{}, std::false_type{});
+  if (kt < nk) step(kt, std::false_type{}, std::false_type{});
 
-  // ---- epilogue.  acc[jc][it][j]: token row0 + 128 wt + 32 it + n, column
+  // ---- epilogue.  acc[jc][it][j]: token row0 + 64 wt + 32 it + n, column
   // col0 + 128 wc + 32 jc + 8 (j / 4) + 4 hg + j % 4.
   const int ccol = col0 + 128 * wc;  // the wave's first column (a head block in the qkv form)
   if (ccol >= a.N) return;
   if constexpr (EPI == kGemmPlain) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int64_t tok = row0 + 128 * wt + 32 * it + n;
+    for (int it = 0; it < 2; ++it) {
+      const int64_t tok = row0 + 64 * wt + 32 * it + n;
       if (tok >= a.M) continue;
       uint16_t* dst = a.y + tok * a.ldy + ccol + 4 * hg;
 #pragma unroll
@@ -175,8 +215,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
     // norm scale of column 32 jc + 8 (j / 4) + 4 hg + j % 4
     auto gk = [&](int jc, int j) __attribute__((always_inline)) { return gk_lds[32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)]; };
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int64_t tok = row0 + 128 * wt + 32 * it + n;
+    for (int it = 0; it < 2; ++it) {
+      const int64_t tok = row0 + 64 * wt + 32 * it + n;
       const bool valid = tok < a.M;
       float x[4][16];
 #pragma unroll
@@ -250,7 +290,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
       hipFuncSetAttribute((const void*)k_gemm<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemQkv);
   if (attr != hipSuccess) return attr;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_gemm<EPI>, dim3((unsigned)tiles), dim3(256), kSmemQkv, st, a);
+  hipLaunchKernelGGL(k_gemm<EPI>, dim3((unsigned)tiles), dim3(kThreads), kSmemQkv, st, a);
   return hipGetLastError();
 }
 

@@ -9,11 +9,12 @@ One step = the whole hot path on synthetic Qwen3-shaped inputs resident in HBM:
     the combine.
 Prints one JSON line.  ``value`` is prefill attention TFLOP/s (algorithmic flops:
 unmasked causal pairs only); the decode KV-read GB/s sits under ``decode``.
-Besides the step, the line carries chunked-prefill (``append``) and the gated
-head_dim-256 layer of Qwen3-Next (``gated``: prefill and decode) figures.
+Besides the step, the line carries chunked-prefill (``append``), the gated
+head_dim-256 layer of Qwen3-Next (``gated``: prefill and decode) and the whole
+attention sublayer with its projections (``layer``) figures.
 
     python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--no-decode]
-                    [--no-cpu-baseline] [--no-append] [--no-gated] [--gpus 1]
+                    [--no-cpu-baseline] [--no-append] [--no-gated] [--no-layer] [--gpus 1]
 """
 
 import argparse
@@ -292,6 +293,54 @@ def measure_gated(dev, n_calls=10):
     return res
 
 
+def measure_layer(dev, n_calls=10):
+    """The whole attention sublayer of Qwen3-8B (hidden 4096, 32 / 8 heads) on
+    the 4 x 4096 prefill with the cache write: the fused q/k/v projection, the
+    core and o_proj in one qwattn_attention_layer call; the o_proj GEMM is also
+    timed on its own through qwattn_linear."""
+    import torch
+    from attention_qk_norm_amd import accounting, binding as B, inputs
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+    spec = inputs.layer_case_spec()
+    hidden = inputs.LAYER_HIDDEN[spec.case_id]
+    log(f"sublayer workload: {spec.workload}")
+    w_qkv, w_o = inputs.layer_weights(spec, hidden)
+    x = up(inputs.layer_x(spec, hidden))
+    w_qkv, w_o = up(w_qkv), up(w_o)
+    gq, gk = (up(g) for g in inputs.gammas(spec))
+    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    cu_h = spec.cu_seqlens()
+    cu = torch.from_numpy(cu_h).to(dev)
+    kc = torch.empty(spec.n_seq, spec.n_kv_heads, max(spec.lengths), 128, dtype=bf, device=dev)
+    vc = torch.empty_like(kc)
+    y = torch.empty(spec.n_tok, hidden, dtype=bf, device=dev)
+    ws = torch.empty(B.attention_layer_workspace_size(p, B.BF16, hidden, spec.n_seq, spec.n_tok, max(spec.lengths),
+                                                      True), dtype=torch.uint8, device=dev)
+    run = lambda: B.attention_layer(p, x, w_qkv, w_o, gq, gk, cu, cu_h, y=y, k_cache=kc, v_cache=vc, workspace=ws)
+    for _ in range(2):
+        run()
+    c_ms, qkv_ms = _timed(run, n_calls)
+    o_in = torch.empty(spec.n_tok, spec.n_q_heads * 128, dtype=bf, device=dev).normal_()
+    run_o = lambda: B.linear(o_in, w_o, y=y)
+    run_o()
+    _, o_ms = _timed(run_o, n_calls)
+    d = 128
+    qkv_flops = 2 * spec.n_tok * hidden * (spec.n_q_heads + 2 * spec.n_kv_heads) * d
+    o_flops = 2 * spec.n_tok * spec.n_q_heads * d * hidden
+    attn_flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    total = qkv_flops + attn_flops + o_flops
+    gemm = lambda f, ms: {"achieved": round(f / (ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(f / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "kernel_ms": round(ms, 4), "algorithmic_flops": f}
+    return {"metric": "attention sublayer TFLOP/s (q/k/v projection + core + o_proj)", "unit": "TFLOP/s",
+            "workload": spec.workload, "value": round(total / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
+            "algorithmic_flops": total,
+            "roofline": dict(kernel="k_gemm<qkv> (fused q/k/v projection)", bound="mfma", **gemm(qkv_flops, qkv_ms),
+                             traffic=None),
+            "o_proj": dict(kernel="k_gemm<plain> via qwattn_linear", bound="mfma", **gemm(o_flops, o_ms))}
+
+
 def cpu_baseline_prefill(spec, n_sample=3):
     """The oracle, as it stands, on a bounded sample of the prefill workload:
     the first `n_sample` whole sequences of the packed batch (all query heads,
@@ -333,6 +382,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the chunked-prefill (append) measurement")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-layer (head_dim 256) measurements")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-sublayer (projections) measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -421,11 +471,15 @@ def main():
     if not args.no_append:
         log("append (chunked prefill) measurement")
         rec["append"] = measure_append(dev)
+    del pre, dec
     if not args.no_gated:
-        del pre, dec
         torch.cuda.empty_cache()
         log("gated-layer measurements")
         rec["gated"] = measure_gated(dev)
+    if not args.no_layer:
+        torch.cuda.empty_cache()
+        log("sublayer measurement")
+        rec["layer"] = measure_layer(dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
