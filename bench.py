@@ -289,7 +289,7 @@ def measure_gated(dev, n_calls=10):
         "value": round(kv / (c_ms * 1e-3) / 1e9, 1), "call_ms": round(c_ms, 4), "kv_read_bytes": kv,
         "roofline": {"kernel": "k_decode_split", "bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kv / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel_ms": round(k_ms, 4)}}
+                     "traffic": recorded_traffic("k_decode_split_256", "k_decode.hip"), "kernel_ms": round(k_ms, 4)}}
     return res
 
 
@@ -337,8 +337,21 @@ def measure_layer(dev, n_calls=10):
             "workload": spec.workload, "value": round(total / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
             "algorithmic_flops": total,
             "roofline": dict(kernel="k_gemm<qkv> (fused q/k/v projection)", bound="mfma", **gemm(qkv_flops, qkv_ms),
-                             traffic=None),
-            "o_proj": dict(kernel="k_gemm<plain> via qwattn_linear", bound="mfma", **gemm(o_flops, o_ms))}
+                             traffic=recorded_traffic("k_gemm_qkv", "k_gemm.hip")),
+            "o_proj": dict(kernel="k_gemm<plain> via qwattn_linear", bound="mfma", **gemm(o_flops, o_ms),
+                           traffic=recorded_traffic("k_gemm_plain", "k_gemm.hip"))}
+
+
+def copy_calibration(dev):
+    """One 1 GiB device-to-device copy, whose counter readings scale the
+    FETCH_SIZE / WRITE_SIZE figures of a counter run."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"read": 1 << 30, "write": 1 << 30}
 
 
 def cpu_baseline_prefill(spec, n_sample=3):
@@ -383,6 +396,8 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the chunked-prefill (append) measurement")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-layer (head_dim 256) measurements")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-sublayer (projections) measurement")
+    ap.add_argument("--only", choices=["append", "gated", "layer"],
+                    help="profiling aid: run only this measurement and print its record (no step, not a bench line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -395,6 +410,12 @@ def main():
     from attention_qk_norm_amd import accounting, binding as B
     B.load()
     dev = torch.device("cuda:0")
+    if args.only:
+        rec = {"append": measure_append, "gated": measure_gated, "layer": measure_layer}[args.only](dev)
+        if args.copy_calibration:
+            rec["copy_calibration_bytes"] = copy_calibration(dev)
+        print(json.dumps({args.only: rec}), flush=True)
+        return
     pre = setup_prefill(args.prefill_case, dev)
     dec = None if args.no_decode else setup_decode(args.decode_case, dev)
     ev = HipEvents()
@@ -481,13 +502,7 @@ def main():
         log("sublayer measurement")
         rec["layer"] = measure_layer(dev)
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = {"read": 1 << 30, "write": 1 << 30}
-        del src, dst
+        rec["copy_calibration_bytes"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline_prefill(spec)
