@@ -28,11 +28,13 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# Per-source extra flags.  The prefill kernels keep their MFMA accumulators in
-# arch VGPRs: the softmax reads every score with VALU, and the AGPR form made
-# the compiler shuttle the query fragments and scores between register files.
+# Per-source extra flags.  The attention kernels keep their MFMA accumulators
+# in arch VGPRs: the softmax reads every score, and the online softmax rescales
+# every output accumulator, with VALU; the AGPR form made the compiler shuttle
+# them between register files.
 SOURCE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "k_prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "k_prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "k_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, objdir, extra=()):

@@ -13,8 +13,9 @@
 // (A = K rows loaded straight from HBM as 16-byte fragments, B = the g <= 16
 // query heads of the group, resident), so each lane owns one head column and
 // the softmax is lane-local plus two lane swaps.  The probabilities, rounded to
-// bf16, are the B operand of O^T = V^T P^T; V goes HBM -> registers -> the
-// wave's own LDS slot and comes back transposed through ds_read_b64_tr_b16.
+// bf16, are the B operand of O^T = V^T P^T; V goes HBM -> the wave's own LDS
+// slot directly (no staging registers) and comes back transposed through
+// ds_read_b64_tr_b16.
 // Every K and V byte is read once, in 16-byte lane loads.  The gated layers
 // ("第 20 章 Qwen3 与 Qwen3.5" §20.4) multiply the merged output by sigmoid of
 // the gate in the merge kernel.
@@ -37,6 +38,17 @@ __device__ __forceinline__ int v_swz(int row, int chunk) {
 template <int D>
 constexpr int decode_smem_bytes() {
   return 4 * kBlockKeys * 2 * D + 4 * 2 * 16 * 4;
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (lane l's bytes land at
+// lds_base + 16 l; M0 holds the wave-uniform base, one wait state after
+// writing it).  Inline assembly, so the compiler does not wait for every
+// outstanding copy before each LDS read; the loop waits for its own copies.
+__device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
 }
 
 template <int D>
@@ -67,7 +79,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   }
   const uint16_t* kb = a.k_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
   const uint16_t* vb = a.v_cache + (int64_t)i * a.cs_seq + u * a.cs_head;
-  lds_u8* vs = (lds_u8*)(smem) + w * kBlockKeys * 2 * D;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // w is wave-uniform: keep it (and b0) in SGPRs
+  lds_u8* vs = (lds_u8*)(smem) + wu * kBlockKeys * 2 * D;
+  const uint32_t vs_lds = (uint32_t)(uintptr_t)vs;
 
   f32x4 o[D / 16];
 #pragma unroll
@@ -79,7 +93,26 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   const int v_row = 4 * q4 + (lam >> 2);
   const int v_col = 4 * (lam & 3);  // + 16 db, elements
 
-  for (int b0 = kbeg + w * kBlockKeys; b0 < kend; b0 += 4 * kBlockKeys) {
+  for (int b0 = kbeg + wu * kBlockKeys; b0 < kend; b0 += 4 * kBlockKeys) {
+    // V rows of the block go HBM -> this wave's LDS slot directly, in the
+    // swizzled layout: copy m fills LDS bytes 1024 m + 16 lane, i.e. row r,
+    // chunk position cp, which holds global chunk cp ^ ((r & 7) << 1).  Keys
+    // past kend repeat the last key (masked below, and finite).  Issued first:
+    // the K loads after them complete later, so the wait the compiler puts in
+    // front of the score MFMAs also covers these copies.
+    {
+      constexpr int CPR = D / 8;  // 16-byte chunks per row
+      const char* vblk = (const char*)(vb + (int64_t)b0 * a.cs_tok);
+      const int last = kend - 1 - b0;
+#pragma unroll
+      for (int m = 0; m < D / 16; ++m) {
+        const int o = 1024 * m + 16 * lane;
+        const int r = o / (2 * D), cp = (o % (2 * D)) / 16;
+        const int c = cp ^ ((r & 7) << 1);
+        load_lds16_async(vs_lds + 1024 * m, vblk, (uint32_t)(min(r, last) * a.cs_tok * 2) + c * 16);
+      }
+      static_assert(CPR * 16 == 2 * D, "row bytes");
+    }
     // K fragments: A[m = key b0 + 16 sb + hh][k = dim 32kk + 8 q4 + e]
     u32x4 kr[2][KF];
 #pragma unroll
@@ -90,16 +123,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
         kr[sb][kk] = key < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * a.cs_tok + 32 * kk + 8 * q4)
                                 : u32x4{0, 0, 0, 0};
     }
-    // V rows of the block: lane chunk c = lane + 64 m -> row c / (D/8), 16-byte chunk c % (D/8)
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    u32x4 vr[D / 16];
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      const int c = lane + 64 * m;
-      const int key = b0 + c / CPR;
-      vr[m] = key < kend ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * a.cs_tok + (c % CPR) * 8)
-                         : u32x4{0, 0, 0, 0};
-    }
     f32x4 sacc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -109,16 +132,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
         sacc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[sb][kk]), qf[kk],
                                                           sacc[sb], 0, 0, 0);
     }
-    // stage V in this wave's LDS slot (only this wave reads it)
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      const int c = lane + 64 * m;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(vs + v_swz<D>(c / CPR, c % CPR)) = vr[m];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // this wave's V copies have landed (only this wave reads its slot)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     // softmax over the block: sacc[sb][j] = key b0 + 16sb + 4q4 + j of head hh
     float sv[8];
