@@ -312,6 +312,88 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
     }
   };
 
+  // Static-bound tile in a fixed issue order (the weights need no row
+  // maximum, so they can form while MFMAs run):
+  //   S(keys 0-31) | S(keys 32-63) + weights(0-31) | PV(0-31) + weights(32-63) | PV(32-63)
+  // With one wave per SIMD the issue order is the schedule: every MFMA is
+  // followed by the LDS fragment read needed kLead MFMAs later and, in the
+  // middle phases, by half a weight pair; sched_barrier keeps the compiler
+  // from regrouping them.
+  constexpr int kLead = 6;
+  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag) __attribute__((always_inline)) {
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    f32x16 sacc[2];
+    bf16x8 pf[4];
+    u32x4 w4[2][2];
+    float psum = 0.f;
+    bf16x8 kf[32];  // K fragment (kb, kk) at 16 kb + kk
+    bf16x8 vf[32];  // V fragment (kk, db) at 8 kk + db
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      kf[i] = lds_load_b128(ks + k_base + (i >> 4) * 512 + (i & 15) * 32);
+    };
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int kk = i >> 3, db = i & 7;
+      const lds_u8* vp = vs + v_base + 16 * (kk & 1) * kVBlk + (kk >> 1) * 512 + db * 64;
+      vf[i] = concat_tr16(lds_read_tr16(vp), lds_read_tr16(vp + 8 * kVBlk));
+    };
+    // fragment read r of the tile's stream: K fragments 0..31, then V 0..31
+    auto fread = [&](int r) __attribute__((always_inline)) {
+      if (r < 32) kread(r);
+      else if (r < 64) vread(r - 32);
+    };
+    auto smfma = [&](int kb, int kk) __attribute__((always_inline)) {
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[16 * kb + kk], qf[kk], kk == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+    };
+    auto pmfma = [&](int i) __attribute__((always_inline)) {
+      o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i >> 3], o[i & 7], 0, 0, 0);
+    };
+    // Weight pair m (0..7) of key block kb: registers j = 2m, 2m+1 of sacc[kb],
+    // keys key0 + 32kb + 8(j/4) + 4hg + j%4; slice 2kb + j/8 of P^T.
+    auto weights = [&](int kb, int m) __attribute__((always_inline)) {
+      const int j = 2 * m, h = j >> 3, e = (j & 7) >> 1;
+      float x0 = sacc[kb][j], x1 = sacc[kb][j + 1];
+      if constexpr (kDiag) {  // key > qpos  <=>  constant > lim
+        const int lim = qpos - key0 - 4 * hg - 32 * kb;
+        if (8 * (j >> 2) + (j & 3) > lim) x0 = -INFINITY;
+        if (8 * ((j + 1) >> 2) + ((j + 1) & 3) > lim) x1 = -INFINITY;
+      }
+      w4[kb][h][e] = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
+      psum = sum_bf16x2(w4[kb][h][e], psum);
+      if (e == 3) pf[2 * kb + h] = __builtin_bit_cast(bf16x8, w4[kb][h]);
+    };
+#pragma unroll
+    for (int r = 0; r < kLead; ++r) fread(r);
+    fence();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {  // S(keys 0-31)
+      smfma(0, kk);
+      fread(kk + kLead);
+      fence();
+    }
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {  // S(keys 32-63) + weights of keys 0-31
+      smfma(1, kk);
+      if (kk & 1) weights(0, kk >> 1);
+      fread(16 + kk + kLead);
+      fence();
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // PV(keys 0-31) + weights of keys 32-63
+      pmfma(i);
+      if (i & 1) weights(1, i >> 1);
+      fread(32 + i + kLead);
+      fence();
+    }
+#pragma unroll
+    for (int i = 16; i < 32; ++i) {  // PV(keys 32-63)
+      pmfma(i);
+      fread(32 + i + kLead);
+      fence();
+    }
+    l_run += psum;
+  };
+
   auto run = [&](auto static_tag) __attribute__((always_inline)) {
     for (int t = 0; t < n_tiles; ++t) {
       // Only tile t's copies are outstanding here; once this thread's part
@@ -323,10 +405,18 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
       const int key0 = t * kTileKeys;
       if (key0 > wave_max) continue;  // every key of the tile is in this wave's future
       const lds_u8* ks = lds + (t & 1) * kStageBytes;
-      if (key0 + kTileKeys - 1 > wave_min)
-        tile(ks, ks + kKTile, key0, static_tag, std::true_type{});
-      else
-        tile(ks, ks + kKTile, key0, static_tag, std::false_type{});
+      constexpr bool kStatic = decltype(static_tag)::value;
+      if constexpr (kStatic) {
+        if (key0 + kTileKeys - 1 > wave_min)
+          static_tile(ks, ks + kKTile, key0, std::true_type{});
+        else
+          static_tile(ks, ks + kKTile, key0, std::false_type{});
+      } else {
+        if (key0 + kTileKeys - 1 > wave_min)
+          tile(ks, ks + kKTile, key0, static_tag, std::true_type{});
+        else
+          tile(ks, ks + kKTile, key0, static_tag, std::false_type{});
+      }
     }
   };
   if (use_static)
