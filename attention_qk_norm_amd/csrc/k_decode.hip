@@ -45,7 +45,7 @@ constexpr int decode_smem_bytes() {
 // writing it).  Inline assembly, so the compiler does not wait for every
 // outstanding copy before each LDS read; the loop waits for its own copies.
 __device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :
                : "s"(lds_base), "v"(voff), "s"(gbase)
                : "memory", "m0");
@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
       const int key = b0 + 16 * sb + hh;
 #pragma unroll
       for (int kk = 0; kk < KF; ++kk)
-        kr[sb][kk] = key < kend ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * a.cs_tok + 32 * kk + 8 * q4)
+        kr[sb][kk] = key < kend ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                      kb + (int64_t)key * a.cs_tok + 32 * kk + 8 * q4))
                                 : u32x4{0, 0, 0, 0};
     }
     f32x4 sacc[2];
