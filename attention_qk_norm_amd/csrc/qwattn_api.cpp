@@ -270,7 +270,7 @@ size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype d
   if (check_params(params, dtype) || n_seq < 0 || n_tok < 0 || max_seqlen < 0) return 0;
   const int g = params->n_q_heads / params->n_kv_heads;
   const int bm = std::max(1, prefill_rows(params, dtype) / g);
-  const int max_tiles = (max_seqlen + bm - 1) / bm;
+  const int max_tiles = (int)(((int64_t)max_seqlen + bm - 1) / bm);
   const int64_t n_items = n_tok / bm + n_seq;
   return prefill_layout(params, dtype, n_seq, n_tok, max_tiles, n_items, with_cache != 0).total;
 }
@@ -327,7 +327,7 @@ qwattn_status check_sequences(const qwattn_params* params, qwattn_dtype dtype, c
   sp.n_tok = cu_seqlens_host[n_seq];
   sp.bm = std::max(1, rows / g);
   for (int s = 0; s < n_seq; ++s) {
-    const int nt = (cu_seqlens_host[s + 1] - cu_seqlens_host[s] + sp.bm - 1) / sp.bm;
+    const int nt = (int)(((int64_t)cu_seqlens_host[s + 1] - cu_seqlens_host[s] + sp.bm - 1) / sp.bm);
     sp.max_tiles = std::max(sp.max_tiles, nt);
     sp.n_items += nt;
   }
@@ -712,7 +712,7 @@ size_t qwattn_attention_layer_workspace_size(const qwattn_params* params, qwattn
   if (check_layer_params(params, dtype, hidden) || n_seq < 0 || n_tok < 0 || max_seqlen < 0) return 0;
   const int g = params->n_q_heads / params->n_kv_heads;
   const int bm = std::max(1, prefill_rows(params, dtype) / g);
-  const int max_tiles = (max_seqlen + bm - 1) / bm;
+  const int max_tiles = (int)(((int64_t)max_seqlen + bm - 1) / bm);
   return layer_layout(params, n_seq, n_tok, max_tiles, n_tok / bm + n_seq, with_cache != 0).total;
 }
 
