@@ -75,6 +75,12 @@ def load(path=None):
     lib.qwattn_attention_layer.restype = i32
     lib.qwattn_attention_layer_workspace_size.argtypes = [pp, i32, i32, i32, i64, i32, i32]
     lib.qwattn_attention_layer_workspace_size.restype = sz
+    lib.qwattn_mfma_probe.argtypes = [i32, vp, vp]
+    lib.qwattn_mfma_probe.restype = i32
+    lib.qwattn_mfma_probe_flops.argtypes = [i32]
+    lib.qwattn_mfma_probe_flops.restype = ctypes.c_double
+    lib.qwattn_hbm_read_probe.argtypes = [vp, i64, vp, vp]
+    lib.qwattn_hbm_read_probe.restype = i32
     lib.qwattn_status_str.argtypes = [i32]
     lib.qwattn_status_str.restype = ctypes.c_char_p
     lib.qwattn_last_error.argtypes = []
@@ -298,6 +304,32 @@ def linear(x, w, y=None):
         y = torch.empty(m, n, dtype=x.dtype, device=x.device)
     _check(lib.qwattn_linear(_dtype_code(x), _ptr(x), _ptr(w), m, n, k, _ptr(y), _stream()))
     return y
+
+
+def mfma_probe(iters, sink):
+    """Measurement aid: the register-only MFMA loop (see qwattn.h); sink is a
+    float32 device tensor of at least one element."""
+    lib = load()
+    _dev(sink, "sink")
+    _check(lib.qwattn_mfma_probe(iters, _ptr(sink), _stream()))
+
+
+def mfma_probe_flops(iters):
+    return load().qwattn_mfma_probe_flops(iters)
+
+
+def hbm_read_probe(src, sink, nbytes=None):
+    """Measurement aid: reads nbytes (default: all of src, rounded down to 16)
+    of the device tensor src once with nontemporal loads."""
+    lib = load()
+    _dev(src, "src")
+    _dev(sink, "sink")
+    total = src.numel() * src.element_size()
+    nbytes = (total if nbytes is None else nbytes) // 16 * 16
+    if nbytes > total:
+        raise ValueError("nbytes exceeds src")
+    _check(lib.qwattn_hbm_read_probe(_ptr(src), nbytes, _ptr(sink), _stream()))
+    return nbytes
 
 
 def attention_layer_workspace_size(params, dtype_code, hidden, n_seq, n_tok, max_seqlen, with_cache):

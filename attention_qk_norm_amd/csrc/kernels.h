@@ -161,4 +161,8 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t st);
 
+// ---------------------------------------------------------------- measurement aids
+hipError_t launch_mfma_probe(int n_wg, int iters4, float* sink, hipStream_t st);
+hipError_t launch_read_probe(int n_wg, const void* src, int64_t n16, float* sink, hipStream_t st);
+
 }  // namespace qw

@@ -53,6 +53,14 @@ int q_row(const qwattn_params* p) { return p->output_gate ? 2 * p->head_dim : p-
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Compute units of the current device.
+hipError_t cu_count(int* n) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+  return e;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int elem_bytes(qwattn_dtype dt) { return dt == QWATTN_BF16 ? 2 : 4; }
@@ -688,6 +696,40 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
     if ((e = timed_launch(strm, [&] { return qw::launch_attn_f32(a, n_seq, strm); })) != hipSuccess)
       return hip_fail(e, "decode attention launch");
   }
+  return QWATTN_OK;
+}
+
+qwattn_status qwattn_mfma_probe(int32_t iters, float* sink, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if (iters <= 0) return fail(QWATTN_ERR_INVALID_ARG, "iters must be positive");
+  if ((st = check_ptr(sink, "sink", 4))) return st;
+  int n_cu = 0;
+  if (const hipError_t e = cu_count(&n_cu)) return hip_fail(e, "device query");
+  hipStream_t strm = (hipStream_t)stream;
+  const hipError_t e =
+      timed_launch(strm, [&] { return qw::launch_mfma_probe(n_cu, (int)(((int64_t)iters + 3) / 4), sink, strm); });
+  if (e != hipSuccess) return hip_fail(e, "MFMA probe launch");
+  return QWATTN_OK;
+}
+
+double qwattn_mfma_probe_flops(int32_t iters) {
+  int n_cu = 0;
+  if (iters <= 0 || cu_count(&n_cu) != hipSuccess) return 0.0;
+  // workgroups x 4 waves x rounds x 32 MFMAs x 32 x 32 x 16 x 2 flops
+  return (double)n_cu * 4 * ((((int64_t)iters + 3) / 4) * 32) * 32768.0;
+}
+
+qwattn_status qwattn_hbm_read_probe(const void* src, int64_t bytes, float* sink, void* stream) {
+  g_last_error.clear();
+  qwattn_status st;
+  if (bytes <= 0 || bytes % 16) return fail(QWATTN_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if ((st = check_ptr(src, "src")) || (st = check_ptr(sink, "sink", 4))) return st;
+  int n_cu = 0;
+  if (const hipError_t e = cu_count(&n_cu)) return hip_fail(e, "device query");
+  hipStream_t strm = (hipStream_t)stream;
+  const hipError_t e = timed_launch(strm, [&] { return qw::launch_read_probe(32 * n_cu, src, bytes / 16, sink, strm); });
+  if (e != hipSuccess) return hip_fail(e, "HBM read probe launch");
   return QWATTN_OK;
 }
 

@@ -75,6 +75,34 @@ def recorded_traffic(kernel, source):
     return None
 
 
+def measure_peaks(dev, src):
+    """The MFMA rate and HBM read bandwidth this GPU sustains in this run (the
+    library's measurement aids, best of 3, timed with the library's hook): a
+    register-only MFMA loop on every SIMD, and one nontemporal read of `src`."""
+    import torch
+    from attention_qk_norm_amd import binding as B
+    ev = HipEvents()
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def best_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(3):
+            a, b = ev.create(), ev.create()
+            B.set_timing_events(a, b)
+            fn()
+            torch.cuda.synchronize()
+            ms.append(ev.elapsed_ms(a, b))
+        return min(ms)
+
+    iters = 20000
+    mfma = B.mfma_probe_flops(iters) / best_ms(lambda: B.mfma_probe(iters, sink)) / 1e9
+    nbytes = B.hbm_read_probe(src, sink)
+    hbm = nbytes / best_ms(lambda: B.hbm_read_probe(src, sink)) / 1e6
+    return {"mfma_tflops": round(mfma, 1), "hbm_read_gbs": round(hbm, 1), "hbm_read_bytes": nbytes}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -450,6 +478,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    log("measured peaks (MFMA loop, streaming read)")
+    # the read source must dwarf the 256 MB Infinity Cache: the decode K cache
+    # (4.3 GB at the 64-sequence workload), else a temporary 2 GiB buffer
+    peaks = measure_peaks(dev, dec["kc"] if dec is not None else torch.ones(1 << 29, dtype=torch.int32, device=dev))
+
     spec = pre["spec"]
     flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
     attn_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pre_ev]))
@@ -471,7 +504,11 @@ def main():
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip") if args.prefill_case == 1 else None,
-                     "kernel_ms": round(attn_ms, 4), "algorithmic_flops": flops},
+                     "kernel_ms": round(attn_ms, 4), "algorithmic_flops": flops,
+                     "measured_peak": {"value": peaks["mfma_tflops"], "unit": "TFLOP/s",
+                                       "frac": round(achieved / peaks["mfma_tflops"], 4),
+                                       "how": "register-only v_mfma_f32_32x32x16_bf16 loop, one wave per SIMD on "
+                                              "every CU, this run (qwattn_mfma_probe)"}},
     }
     if dec is not None:
         ds = dec["spec"]
@@ -487,7 +524,11 @@ def main():
                          "achieved": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("k_decode_split", "k_decode.hip") if args.decode_case == 2 else None,
-                         "kernel_ms": round(split_ms, 4)},
+                         "kernel_ms": round(split_ms, 4),
+                         "measured_peak": {"value": peaks["hbm_read_gbs"], "unit": "GB/s",
+                                           "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / peaks["hbm_read_gbs"], 4),
+                                           "how": f"one nontemporal streaming read of {peaks['hbm_read_bytes']} bytes "
+                                                  "(the K cache), this run (qwattn_hbm_read_probe)"}},
         }
     if not args.no_append:
         log("append (chunked prefill) measurement")

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define QWATTN_ABI_VERSION 4
+#define QWATTN_ABI_VERSION 5
 #define QWATTN_HEAD_DIM 128        /* Qwen3 layers                  */
 #define QWATTN_HEAD_DIM_GATED 256  /* gated Qwen3-Next / 3.5 layers */
 
@@ -267,6 +267,30 @@ size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dt
  * fused q/k/v projection of the sublayer) and `end` right after it, then clears
  * the hook.  Setting it enqueues nothing. */
 qwattn_status qwattn_set_timing_events(void* begin, void* end);
+
+/* ---- Measurement aids (not part of the attention path).  Reporting the
+ * attention kernels against the rate this GPU sustains right now, beside the
+ * published peaks: under a full MFMA load the clock sits well below its
+ * maximum.  Both launch on `stream` and honour the timing hook above (begin
+ * and end bracket the probe kernel); time them with it.  `sink` is device
+ * memory of at least one float that the probe may write (only to keep its
+ * work from being optimised away); it enqueues nothing else.
+ *
+ * qwattn_mfma_probe: on every compute unit one workgroup of four waves (one
+ * per SIMD) runs a register-only loop of v_mfma_f32_32x32x16_bf16 over 8
+ * independent accumulators, operands bf16 values that look random, iters
+ * rounded up to a multiple of 4 (> 0 required).  Its work in flops is
+ * qwattn_mfma_probe_flops(iters) (0 when the device cannot be queried).
+ *
+ * qwattn_hbm_read_probe: reads `bytes` (> 0, a multiple of 16) of device
+ * memory at `src` (16-byte aligned) once with 16-byte nontemporal loads, eight
+ * in flight per lane.
+ *
+ * Errors: QWATTN_ERR_INVALID_ARG (checked before anything is enqueued),
+ * QWATTN_ERR_HIP on a failed launch or device query. */
+qwattn_status qwattn_mfma_probe(int32_t iters, float* sink, void* stream);
+double qwattn_mfma_probe_flops(int32_t iters);
+qwattn_status qwattn_hbm_read_probe(const void* src, int64_t bytes, float* sink, void* stream);
 
 const char* qwattn_status_str(qwattn_status status); /* static string             */
 const char* qwattn_last_error(void);                 /* this thread's last detail */

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qwattn_abi_version() == 4
+    assert lib.qwattn_abi_version() == 5
     for st in range(6):
         assert lib.qwattn_status_str(st)
 
@@ -187,3 +187,17 @@ def test_qk_norm_rope_validation(lib):
     assert f(ctypes.byref(p), 1, F, None, F, F, F, 10, None, None, None) == B.ERR_INVALID_ARG
     assert f(ctypes.byref(p), 1, F, None, F, None, F, -1, F, None, None) == B.ERR_INVALID_ARG
     assert f(ctypes.byref(p), 1, F, None, F, None, F, 0, F, None, None) == B.OK
+
+
+def test_probe_validation(lib):
+    """The measurement aids reject bad arguments before any device query."""
+    assert lib.qwattn_mfma_probe(0, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_mfma_probe(-4, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_mfma_probe(16, None, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_mfma_probe(16, ODD, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_mfma_probe_flops(0) == 0.0
+    assert lib.qwattn_hbm_read_probe(F, 0, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_hbm_read_probe(F, 24, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_hbm_read_probe(None, 1 << 20, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_hbm_read_probe(ODD, 1 << 20, F, None) == B.ERR_INVALID_ARG
+    assert lib.qwattn_hbm_read_probe(F, 1 << 20, None, None) == B.ERR_INVALID_ARG
