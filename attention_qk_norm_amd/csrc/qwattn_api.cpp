@@ -180,9 +180,12 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
 }
 
 // ------------------------------------------------------------------ decode plan
+// Keys per split-K chunk: the largest that still gives about 2048 workgroups
+// (a few per CU); larger chunks spread each workgroup's fixed work (query
+// load, merge, partial write) over more keys.
 int decode_chunk(int64_t total_keys, int n_kv_heads) {
   for (int c : {2048, 1024, 512, 256})
-    if ((total_keys / c) * n_kv_heads >= 4096) return c;
+    if ((total_keys / c) * n_kv_heads >= 2048) return c;
   return qw::kDecodeKeysPerPass;
 }
 
