@@ -14,19 +14,21 @@
 //    are.  So K and V reach HBM once, already in their cached form
 //    ("Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE).
 //
-// Tiling: a workgroup (4 waves) computes a 256-token x 256-column tile as
-// C^T = W X^T with v_mfma_f32_32x32x16_bf16 (A = W fragment, B = X fragment,
-// both 16-byte reads from LDS).  Wave w covers 128 tokens ((w >> 1) half) x
-// 128 columns ((w & 1) half: exactly one head block), as 4 x 4 accumulators of
-// 32 x 32.  In the transposed accumulator a lane owns ONE token (lane % 32) and
-// 64 of the head block's 128 columns (the other 64 sit in lane ^ 32), and
-// columns c and c + 64 (a RoPE pair) share a lane, so the norm is a lane-local
-// sum plus one lane-pair exchange and the rotation is register-local.
+// Tiling: a workgroup (8 waves, two per SIMD) computes a 256-token x
+// 256-column tile as C^T = W X^T with v_mfma_f32_32x32x16_bf16 (A = W
+// fragment, B = X fragment, both 16-byte reads from LDS).  Wave w covers 64
+// tokens ((w >> 1) quarter) x 128 columns ((w & 1) half: exactly one head
+// block), as 4 x 2 accumulators of 32 x 32.  In the transposed accumulator a
+// lane owns ONE token (lane % 32) and 64 of the head block's 128 columns (the
+// other 64 sit in lane ^ 32), and columns c and c + 64 (a RoPE pair) share a
+// lane, so the norm is a lane-local sum plus one lane-pair exchange and the
+// rotation is register-local.
 //
-// K steps of 64: the x and W tiles (256 rows x 128 B each) go HBM -> LDS
-// directly (global_load_lds_dwordx4) into a two-stage ring of padded 1 KB
-// blocks (row r in block r % 32, slot r / 32; 16-byte skew between blocks, so
-// the 16 rows of a fragment read land in 16 distinct bank groups).
+// K steps of 64: the x and W tiles (256 rows x 128 B each) pass through
+// registers into a two-stage LDS ring of padded 1 KB blocks (row r in block
+// r % 32, slot r / 32; 16-byte skew between blocks, so the 16 rows of a
+// fragment read land in 16 distinct bank groups).  Each K step is loaded one
+// step ahead, one 16-byte block per lane after every fourth MFMA.
 #include <type_traits>
 
 #include "kernels.h"
