@@ -16,7 +16,7 @@ Page references used below:
         rotate the new K at start_pos, never re-rotate old K; rectangular mask
         from pos_start), §20.9 (chunked-append equivalence).
 
-Readings where the pages are silent or disagree (each is listed in the design doc):
+Readings where the pages are silent or disagree:
   * order: norm then RoPE ([RL], [NW], [XW], [OZ]); [QA] claims RoPE then norm.
     Both are available through ``order`` (the library too, as params.order).
   * eps sits inside the square root, added to the mean square ([XW] RMSNorm;

@@ -15,7 +15,7 @@ Page references used below:
         uses d_r, not head_dim, as its denominator (head_dim 256 with factor
         0.25 rotates 64 coordinates).
 
-Readings (each listed in the design doc):
+Readings:
   * the rotated coordinates rotate-half among themselves: pairs (i, i + d_r/2)
     for i < d_r/2, frequency theta^(-2i/d_r); coordinates d_r .. d-1 pass;
   * "split inside each head": head h of the q_proj output owns the slice

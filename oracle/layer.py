@@ -16,7 +16,7 @@ Page references used below:
   [NW]  "14. Qwen 家族：从 QKV 偏置到混合注意力", model table: Qwen3 has no QKV
         bias (QK-Norm replaced it); hidden sizes 1024 / 4096 / 5120 ...
 
-Readings (each listed in the design doc):
+Readings:
   * a linear map with weight W [out, in] computes y = x W^T (no bias);
   * head h of a projection output owns the features h*d .. (h+1)*d - 1, and
     the attention output rows of the heads are concatenated in head order
