@@ -485,8 +485,13 @@ def main():
 
     spec = pre["spec"]
     flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
-    attn_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in pre_ev]))
-    pre_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in call_ev]))
+    attn_all = [ev.elapsed_ms(a, b) for a, b in pre_ev]
+    pre_call_all = [e[0].elapsed_time(e[1]) for e in call_ev]
+    attn_ms = float(np.mean(attn_all))
+    pre_call_ms = float(np.mean(pre_call_all))
+
+    def pct(v):  # p10 / median / p90 of the timed iterations, ms
+        return [round(float(x), 4) for x in np.percentile(v, [10, 50, 90])]
     value = flops / (pre_call_ms * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
     rec = {
@@ -499,12 +504,14 @@ def main():
                    "rope_theta": spec.theta, "parallelism": "single-gpu",
                    "decode_workload": None if dec is None else dec["spec"].workload},
         "prefill_call_ms": round(pre_call_ms, 4),
+        "prefill_call_ms_p10_p50_p90": pct(pre_call_all),
         "prefill_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip") if args.prefill_case == 1 else None,
-                     "kernel_ms": round(attn_ms, 4), "algorithmic_flops": flops,
+                     "kernel_ms": round(attn_ms, 4), "kernel_ms_p10_p50_p90": pct(attn_all),
+                     "algorithmic_flops": flops,
                      "measured_peak": {"value": peaks["mfma_tflops"], "unit": "TFLOP/s",
                                        "frac": round(achieved / peaks["mfma_tflops"], 4),
                                        "how": "register-only v_mfma_f32_32x32x16_bf16 loop, one wave per SIMD on "
@@ -513,18 +520,21 @@ def main():
     if dec is not None:
         ds = dec["spec"]
         kv_bytes = accounting.decode_kv_read_bytes(ds.lengths, ds.n_kv_heads)
-        split_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in dec_ev]))
-        dec_call_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in call_ev]))
+        split_all = [ev.elapsed_ms(a, b) for a, b in dec_ev]
+        dec_call_all = [e[2].elapsed_time(e[3]) for e in call_ev]
+        split_ms = float(np.mean(split_all))
+        dec_call_ms = float(np.mean(dec_call_all))
         rec["decode"] = {
             "metric": "decode KV-read GB/s", "unit": "GB/s", "workload": ds.workload,
             "value": round(kv_bytes / (dec_call_ms * 1e-3) / 1e9, 1), "call_ms": round(dec_call_ms, 4),
+            "call_ms_p10_p50_p90": pct(dec_call_all),
             "frac_hbm_peak": round(kv_bytes / (dec_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_read_bytes": kv_bytes,
             "roofline": {"kernel": "k_decode_split", "bound": "hbm",
                          "achieved": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("k_decode_split", "k_decode.hip") if args.decode_case == 2 else None,
-                         "kernel_ms": round(split_ms, 4),
+                         "kernel_ms": round(split_ms, 4), "kernel_ms_p10_p50_p90": pct(split_all),
                          "measured_peak": {"value": peaks["hbm_read_gbs"], "unit": "GB/s",
                                            "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / peaks["hbm_read_gbs"], 4),
                                            "how": f"one nontemporal streaming read of {peaks['hbm_read_bytes']} bytes "
