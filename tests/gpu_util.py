@@ -124,3 +124,38 @@ def oracle_rows(spec, seq, rows, heads):
     gq, gk = inputs.gammas(spec)
     return oracle.attention_prefill_rows(q, k, v, gq, gk, rows, heads, spec.n_q_heads, spec.n_kv_heads,
                                          eps=spec.eps, theta=spec.theta)
+
+
+def append_case(spec, x, splits, cap):
+    """Prefix of each sequence by prefill (cache written), then its remaining
+    tokens as one append.  splits[s] = prefix length of sequence s.  Returns the
+    append output [n_new][Hq][128], the cache and the oracle's output."""
+    dt = torch_dtype(spec)
+    p = params(spec)
+    n = spec.n_seq
+    cu = x["cu_seqlens"]
+    kc = torch.full((n, spec.n_kv_heads, cap, 128), 7.0, dtype=dt, device=DEV)
+    vc = torch.full_like(kc, 7.0)
+    pre = [np.arange(cu[s], cu[s] + splits[s]) for s in range(n)]
+    new = [np.arange(cu[s] + splits[s], cu[s + 1]) for s in range(n)]
+    cu_pre = np.concatenate([[0], np.cumsum([len(r) for r in pre])]).astype(np.int32)
+    cu_new = np.concatenate([[0], np.cumsum([len(r) for r in new])]).astype(np.int32)
+    ip, inew = np.concatenate(pre).astype(np.int64), np.concatenate(new).astype(np.int64)
+    g = lambda name: up(x[name], dt)
+    if cu_pre[-1] > 0:
+        B.prefill(p, up(x["q"][ip], dt), up(x["k"][ip], dt), up(x["v"][ip], dt), g("q_gamma"), g("k_gamma"),
+                  torch.from_numpy(cu_pre).to(DEV), cu_pre, k_cache=kc, v_cache=vc)
+    sp = np.array(splits, dtype=np.int32)
+    out = B.append(p, up(x["q"][inew], dt), up(x["k"][inew], dt), up(x["v"][inew], dt), g("q_gamma"),
+                   g("k_gamma"), kc, vc, torch.from_numpy(sp).to(DEV), torch.from_numpy(cu_new).to(DEV),
+                   sp, cu_new)
+    torch.cuda.synchronize()
+    ref = []
+    for s in range(n):
+        a, b, c = cu[s], cu[s] + splits[s], cu[s + 1]
+        kh = oracle.qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(splits[s]), spec.eps, spec.theta)
+        o, _ = oracle.attention_append(x["q"][b:c], x["k"][b:c], x["v"][b:c], x["q_gamma"], x["k_gamma"], kh,
+                                       x["v"][a:b], splits[s], spec.n_q_heads, spec.n_kv_heads, eps=spec.eps,
+                                       theta=spec.theta)
+        ref.append(o)
+    return out, kc, vc, np.concatenate(ref), cu_new

@@ -261,41 +261,6 @@ def test_prefill_full_size_sampled(case_id):
 
 # ------------------------------------------------------------------ append (chunked prefill)
 
-def _append_case(spec, x, splits, cap):
-    """Prefix of each sequence by prefill (cache written), then its remaining
-    tokens as one append.  splits[s] = prefix length of sequence s.  Returns the
-    append output [n_new][Hq][128], the cache and the oracle's output."""
-    dt = U.torch_dtype(spec)
-    p = U.params(spec)
-    n = spec.n_seq
-    cu = x["cu_seqlens"]
-    kc = torch.full((n, spec.n_kv_heads, cap, 128), 7.0, dtype=dt, device=U.DEV)
-    vc = torch.full_like(kc, 7.0)
-    pre = [np.arange(cu[s], cu[s] + splits[s]) for s in range(n)]
-    new = [np.arange(cu[s] + splits[s], cu[s + 1]) for s in range(n)]
-    cu_pre = np.concatenate([[0], np.cumsum([len(r) for r in pre])]).astype(np.int32)
-    cu_new = np.concatenate([[0], np.cumsum([len(r) for r in new])]).astype(np.int32)
-    ip, inew = np.concatenate(pre).astype(np.int64), np.concatenate(new).astype(np.int64)
-    g = lambda name: U.up(x[name], dt)
-    if cu_pre[-1] > 0:
-        B.prefill(p, U.up(x["q"][ip], dt), U.up(x["k"][ip], dt), U.up(x["v"][ip], dt), g("q_gamma"), g("k_gamma"),
-                  torch.from_numpy(cu_pre).to(U.DEV), cu_pre, k_cache=kc, v_cache=vc)
-    sp = np.array(splits, dtype=np.int32)
-    out = B.append(p, U.up(x["q"][inew], dt), U.up(x["k"][inew], dt), U.up(x["v"][inew], dt), g("q_gamma"),
-                   g("k_gamma"), kc, vc, torch.from_numpy(sp).to(U.DEV), torch.from_numpy(cu_new).to(U.DEV),
-                   sp, cu_new)
-    torch.cuda.synchronize()
-    ref = []
-    for s in range(n):
-        a, b, c = cu[s], cu[s] + splits[s], cu[s + 1]
-        kh = oracle.qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(splits[s]), spec.eps, spec.theta)
-        o, _ = oracle.attention_append(x["q"][b:c], x["k"][b:c], x["v"][b:c], x["q_gamma"], x["k_gamma"], kh,
-                                       x["v"][a:b], splits[s], spec.n_q_heads, spec.n_kv_heads, eps=spec.eps,
-                                       theta=spec.theta)
-        ref.append(o)
-    return out, kc, vc, np.concatenate(ref), cu_new
-
-
 APPEND_CASES = [
     # id, dtype, Hq, Hkv, lengths (prefix + new), prefix lengths
     (140, "bf16", 8, 2, [300, 70, 400, 5], [37, 0, 256, 4]),   # ragged prefixes, one append of a single token
@@ -312,7 +277,7 @@ def test_append_against_cache(cid, dtype, hq, hkv, lengths, splits):
     spec = inputs.custom_spec(cid, dtype, hq, hkv, lengths)
     x = inputs.prefill_inputs(spec)
     U.say(f"append case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths} prefixes={splits}")
-    out, kc, vc, ref, _ = _append_case(spec, x, splits, max(lengths) + 9)
+    out, kc, vc, ref, _ = U.append_case(spec, x, splits, max(lengths) + 9)
     got = U.down(out)
     if dtype == "f32":
         assert np.abs(got - ref).max() <= 1e-4, np.abs(got - ref).max()
