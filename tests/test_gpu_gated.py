@@ -94,6 +94,10 @@ GATED_PREFILL = [
 
 @pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,rot", GATED_PREFILL, ids=[str(c[0]) for c in GATED_PREFILL])
 def test_gated_prefill_small(cid, dtype, hq, hkv, lengths, rot):
+    run_gated_prefill(cid, dtype, hq, hkv, lengths, rot)
+
+
+def run_gated_prefill(cid, dtype, hq, hkv, lengths, rot):
     spec = inputs.gated_spec(cid, dtype, hq, hkv, lengths, rot=rot)
     x = inputs.prefill_inputs(spec)
     U.say(f"gated prefill case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths} rot={rot}")
@@ -214,9 +218,13 @@ GATED_APPEND = [
 
 @pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,splits", GATED_APPEND, ids=[str(c[0]) for c in GATED_APPEND])
 def test_gated_append(cid, dtype, hq, hkv, lengths, splits):
-    spec = inputs.gated_spec(cid, dtype, hq, hkv, lengths, rot=64)
+    run_gated_append(cid, dtype, hq, hkv, lengths, splits, 64)
+
+
+def run_gated_append(cid, dtype, hq, hkv, lengths, splits, rot):
+    spec = inputs.gated_spec(cid, dtype, hq, hkv, lengths, rot=rot)
     x = inputs.prefill_inputs(spec)
-    U.say(f"gated append case {cid} {dtype} lengths={lengths} prefixes={splits}")
+    U.say(f"gated append case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths} prefixes={splits} rot={rot}")
     cu = x["cu_seqlens"]
     qp = q_proj(x)
     kc, vc = _gated_cache(spec, x, [x["k"][cu[s]:cu[s] + splits[s]] for s in range(spec.n_seq)],
@@ -233,10 +241,10 @@ def test_gated_append(cid, dtype, hq, hkv, lengths, splits):
     ref = []
     for s in range(spec.n_seq):
         a, b, c = cu[s], cu[s] + splits[s], cu[s + 1]
-        kh = oracle.gated_qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(splits[s]), spec.eps, spec.theta, 64)
+        kh = oracle.gated_qk_norm_rope(x["k"][a:b], x["k_gamma"], np.arange(splits[s]), spec.eps, spec.theta, rot)
         o, _ = oracle.gated_attention_append(x["q"][b:c], x["gate"][b:c], x["k"][b:c], x["v"][b:c], x["q_gamma"],
                                              x["k_gamma"], kh, x["v"][a:b], splits[s], hq, hkv, eps=spec.eps,
-                                             theta=spec.theta, rot_dim=64)
+                                             theta=spec.theta, rot_dim=rot)
         ref.append(o)
     check(U.down(out), np.concatenate(ref), spec, f"gated append {cid}")
     # the cache holds every token's rotated key and its value, and nothing past the sequence
@@ -260,9 +268,13 @@ GATED_DECODE = [
 
 @pytest.mark.parametrize("cid,dtype,hq,hkv,lengths", GATED_DECODE, ids=[str(c[0]) for c in GATED_DECODE])
 def test_gated_decode(cid, dtype, hq, hkv, lengths):
-    spec = inputs.gated_spec(cid, dtype, hq, hkv, lengths, kind="decode", rot=64)
+    run_gated_decode(cid, dtype, hq, hkv, lengths, 64)
+
+
+def run_gated_decode(cid, dtype, hq, hkv, lengths, rot):
+    spec = inputs.gated_spec(cid, dtype, hq, hkv, lengths, kind="decode", rot=rot)
     x = inputs.decode_new_token(spec)
-    U.say(f"gated decode case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths}")
+    U.say(f"gated decode case {cid} {dtype} Hq={hq} Hkv={hkv} lengths={lengths} rot={rot}")
     raws = inputs.decode_cache_raw_all(spec)
     kc, vc = _gated_cache(spec, x, [r[0] for r in raws], [r[1] for r in raws], max(lengths) + 7)
     dt = U.torch_dtype(spec)
@@ -273,10 +285,10 @@ def test_gated_decode(cid, dtype, hq, hkv, lengths):
     ref = []
     for i, L in enumerate(lengths):
         kr, vr = raws[i]
-        kh = oracle.gated_qk_norm_rope(kr, x["k_gamma"], np.arange(L), spec.eps, spec.theta, 64)
+        kh = oracle.gated_qk_norm_rope(kr, x["k_gamma"], np.arange(L), spec.eps, spec.theta, rot)
         o, _ = oracle.gated_attention_append(x["q"][i:i + 1], x["gate"][i:i + 1], x["k"][i:i + 1],
                                              x["v"][i:i + 1], x["q_gamma"], x["k_gamma"], kh, vr, L, hq, hkv,
-                                             eps=spec.eps, theta=spec.theta, rot_dim=64)
+                                             eps=spec.eps, theta=spec.theta, rot_dim=rot)
         ref.append(o[0])
     check(U.down(out), np.stack(ref), spec, f"gated decode {cid}")
     # the new key and value were appended at start_pos, rotated there
@@ -286,3 +298,67 @@ def test_gated_decode(cid, dtype, hq, hkv, lengths):
         torch.cuda.synchronize()
         assert torch.equal(kc[i, :, L], kh[0])
         assert torch.equal(vc[i, :, L], U.up(x["v"][i], dt))
+
+
+# ------------------------------------------------------------------ seeded shape sweep
+
+# group sizes the head_dim-256 tiles accept (128 bf16 prefill rows, 64 fp32
+# rows, 16 decode rows) and the rotary widths of the boundary
+SWEEP_PREFILL_G = {"bf16": [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24, 32, 64, 128], "f32": [1, 2, 3, 8, 16, 64]}
+SWEEP_DECODE_G = {"bf16": [1, 2, 3, 4, 6, 8, 12, 16], "f32": [1, 3, 8]}
+SWEEP_ROT = [32, 64, 128, 256]
+
+
+def _sweep(kind, n_cases, first_id, dtypes):
+    """Cases drawn from a fixed generator: each dtype walks a shuffled list of
+    group sizes and rotary widths; 1-8 KV heads (at most 128 query heads);
+    ragged lengths with about one empty sequence in ten; at least one new token."""
+    rng = np.random.default_rng([0x6A7E, first_id])
+    table = SWEEP_DECODE_G if kind == "decode" else SWEEP_PREFILL_G
+    g_order = {d: [] for d in dtypes}
+    r_order = {d: [] for d in dtypes}
+    cases = []
+    for i in range(n_cases):
+        dtype = dtypes[i % len(dtypes)]
+        if not g_order[dtype]:
+            g_order[dtype] = [int(v) for v in rng.permutation(table[dtype])]
+        if not r_order[dtype]:
+            r_order[dtype] = [int(v) for v in rng.permutation(SWEEP_ROT)]
+        g, rot = g_order[dtype].pop(), r_order[dtype].pop()
+        hkv = int(rng.choice([h for h in (1, 2, 4, 8) if g * h <= 128]))
+        n_max, l_max = (6, 2500) if kind == "decode" else (4, 500)
+        while True:
+            n = int(rng.integers(1, n_max + 1))
+            lengths = rng.integers(1, l_max + 1, size=n)
+            lengths[rng.random(n) < 0.1] = 0
+            lengths = [int(v) for v in lengths]
+            splits = [int(rng.integers(0, L + 1)) for L in lengths]
+            if kind == "decode" or sum(lengths) - (sum(splits) if kind == "append" else 0) > 0:
+                break
+        extra = (splits,) if kind == "append" else ()
+        cases.append((first_id + i, dtype, g * hkv, hkv, lengths) + extra + (rot,))
+    return cases
+
+
+def _sid(c):
+    return f"{c[0]}-{c[1]}-h{c[2]}x{c[3]}-rot{c[-1]}"
+
+
+SWEEP_PREFILL = _sweep("prefill", 14, 400, ["bf16", "bf16", "bf16", "f32"])
+SWEEP_APPEND = _sweep("append", 6, 430, ["bf16", "bf16", "f32"])
+SWEEP_DECODE = _sweep("decode", 8, 460, ["bf16", "bf16", "bf16", "f32"])
+
+
+@pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,rot", SWEEP_PREFILL, ids=[_sid(c) for c in SWEEP_PREFILL])
+def test_gated_sweep_prefill(cid, dtype, hq, hkv, lengths, rot):
+    run_gated_prefill(cid, dtype, hq, hkv, lengths, rot)
+
+
+@pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,splits,rot", SWEEP_APPEND, ids=[_sid(c) for c in SWEEP_APPEND])
+def test_gated_sweep_append(cid, dtype, hq, hkv, lengths, splits, rot):
+    run_gated_append(cid, dtype, hq, hkv, lengths, splits, rot)
+
+
+@pytest.mark.parametrize("cid,dtype,hq,hkv,lengths,rot", SWEEP_DECODE, ids=[_sid(c) for c in SWEEP_DECODE])
+def test_gated_sweep_decode(cid, dtype, hq, hkv, lengths, rot):
+    run_gated_decode(cid, dtype, hq, hkv, lengths, rot)
