@@ -44,7 +44,11 @@
  *     of a call has the call's dtype, gamma included; math is fp32; outputs
  *     have the input dtype.  Base pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *     on it in order and the call returns without synchronising.
+ *     on it in order and the call returns without synchronising.  Only kernel
+ *     launches (and the optional timing events) are enqueued -- no allocation,
+ *     copy or memset -- so calls may be captured into a HIP graph; launch
+ *     sizes follow the host-side lengths, so a captured graph is valid for the
+ *     lengths it was captured with.
  *   - Every argument is validated before anything is enqueued: on any error the
  *     call returns a non-zero status, launches nothing and writes nothing (the
  *     cache included), as an over-long append must leave the cache and the
