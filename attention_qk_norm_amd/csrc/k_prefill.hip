@@ -214,14 +214,23 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   }
   // The angle is reduced in fp64 (whole turns removed exactly) and evaluated
   // by the hardware sine/cosine, which take turns: errors near 1e-6, far below
-  // the bf16 rounding of the fragments they feed.
+  // the bf16 rounding of the fragments they feed.  Wave w fills angles
+  // 16w .. 16w+15 for every token (lane = token), so the angle index is uniform
+  // and its frequency comes through a scalar load: no vector-memory wait, which
+  // would also wait for the query rows and tiles issued above, precedes it.
   {
-    const double turns = a.rope.w[tid & (kHalf - 1)] * 0.15915494309189535;  // w / (2 pi); one angle per thread
-    for (int e = tid; e < a.bm_tok * kHalf; e += 256) {
-      const double x = (double)(p0 + tok_base + (e >> 6)) * turns;
-      const float r = (float)(x - rint(x));  // in [-1/2, 1/2] turn
-      rope_t[(e >> 6) * kRopeRow + (e & (kHalf - 1))] =
-          make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+    constexpr int kPerWave = kHalf / 4;
+    for (int t0 = 0; t0 < a.bm_tok; t0 += 64) {
+      const int t = t0 + lane;
+      const double pos = (double)(p0 + tok_base + t);
+#pragma unroll
+      for (int k = 0; k < kPerWave; ++k) {
+        const int i = wu * kPerWave + k;
+        const double turns = a.rope.w[i] * 0.15915494309189535;  // w / (2 pi)
+        const double x = pos * turns;
+        const float r = (float)(x - rint(x));  // in [-1/2, 1/2] turn
+        if (t < a.bm_tok) rope_t[t * kRopeRow + i] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+      }
     }
   }
   __syncthreads();
@@ -532,21 +541,42 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   else
     run(std::false_type{});
 
-  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of row (qb, n)
+  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of
+  // row (qb, n).  The normalised rows are staged in LDS (the ring is free once
+  // every wave is past its last tile; no copy is in flight then) and leave as
+  // whole rows: 16 lanes x 16 B per row, and the g heads of a token, adjacent
+  // in out, go out together.  Stored straight from the accumulators, every
+  // store instruction touched 32 rows 2*Hq*128 bytes apart.
+  constexpr int kORow = 2 * kD + 16;  // bytes per staged row (16 B pad)
+  __syncthreads();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float inv_l = 1.0f / pair_sum(l_run[qb]);
-    if (valid[qb]) {
-      uint16_t* dst = (uint16_t*)a.out + ((int64_t)(seq0 + qtok[qb]) * a.Hq + t_head[qb]) * kD;
+    lds_u8* orow = lds + (w * 64 + qb * 32 + n) * kORow;  // row r = hoff * bm_tok + toff
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int d = 32 * db + 8 * jg + 4 * hg;
-          u32x2 pk = {pack_bf16x2(o[qb][db][4 * jg] * inv_l, o[qb][db][4 * jg + 1] * inv_l),
-                      pack_bf16x2(o[qb][db][4 * jg + 2] * inv_l, o[qb][db][4 * jg + 3] * inv_l)};
-          *reinterpret_cast<u32x2*>(dst + d) = pk;
-        }
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d = 32 * db + 8 * jg + 4 * hg;
+        u32x2 pk = {pack_bf16x2(o[qb][db][4 * jg] * inv_l, o[qb][db][4 * jg + 1] * inv_l),
+                    pack_bf16x2(o[qb][db][4 * jg + 2] * inv_l, o[qb][db][4 * jg + 3] * inv_l)};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(orow + 2 * d) = pk;
+      }
+  }
+  __syncthreads();
+  const int n_chunks = a.bm_tok * a.g * (kD / 8);  // 16-byte chunks, ordered (token, head, chunk)
+  // row / g by one multiply: (row + 1/2) / g lies at least 1/(2g) >= 2^-9 from
+  // an integer and the float error is below 2^-15 for row < 256.
+  const float inv_g = 1.0f / (float)a.g;
+#pragma unroll 4
+  for (int c = tid; c < n_chunks; c += 256) {
+    const int row = c >> 4, part = c & 15;
+    const int toff = (int)(((float)row + 0.5f) * inv_g), hoff = row - toff * a.g;
+    if (tok_base + toff < L) {
+      const u32x4 v =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + (hoff * a.bm_tok + toff) * kORow + 16 * part);
+      uint16_t* dst = (uint16_t*)a.out + ((int64_t)(seq0 + tok_base + toff) * a.Hq + u * a.g + hoff) * kD + 8 * part;
+      *reinterpret_cast<u32x4*>(dst) = v;
     }
   }
 }
