@@ -424,28 +424,55 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
   else
     run(std::false_type{});
 
-  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of row n
+  // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of
+  // row n.  The normalised rows are staged in LDS as fp32 (the ring is free
+  // once every wave is past its last tile; no copy is in flight then) and leave
+  // as whole rows, 16 B per lane, the g heads of a token together, with the
+  // gate read the same way.  Straight from the accumulators every gate load and
+  // output store touched 32 rows far apart.  The gate multiplies by a
+  // reciprocal (1 ulp) before the single rounding to bf16.
+  constexpr int kORow = 4 * kW + 16;  // bytes per staged fp32 row (16 B pad)
+  static_assert(128 * kORow <= kSmem, "the staged rows fit in the ring");
   const float inv_l = 1.0f / pair_sum(l_run);
-  if (valid) {
-    const int64_t row = (int64_t)(seq0 + qtok) * a.Hq + t_head;
-    uint16_t* dst = (uint16_t*)a.out + row * kW;
-    const uint16_t* gp = a.gate ? (const uint16_t*)a.gate + row * a.q_row : nullptr;
+  __syncthreads();
+  {
+    lds_u8* orow = lds + r * kORow;  // r = hoff * bm_tok + toff
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int d = 32 * db + 8 * jg + 4 * hg;
-        float y[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] = o[db][4 * jg + c] * inv_l;
-        if (gp) {  // times sigmoid(gate) at the same dims
-          const u32x2 gr = *reinterpret_cast<const u32x2*>(gp + d);
-          const float gv[4] = {bf16_lo(gr[0]), bf16_hi(gr[0]), bf16_lo(gr[1]), bf16_hi(gr[1])};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) y[c] /= 1.0f + __expf(-gv[c]);
-        }
-        *reinterpret_cast<u32x2*>(dst + d) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(orow + 4 * d) =
+            f32x4{o[db][4 * jg] * inv_l, o[db][4 * jg + 1] * inv_l, o[db][4 * jg + 2] * inv_l,
+                  o[db][4 * jg + 3] * inv_l};
       }
+  }
+  __syncthreads();
+  const int n_chunks = a.bm_tok * a.g * (kW / 8);  // 8-dim chunks, ordered (token, head, chunk)
+  // row / g by one multiply: (row + 1/2) / g lies at least 1/(2g) >= 2^-9 from
+  // an integer and the float error is below 2^-15 for row < 256.
+  const float inv_g = 1.0f / (float)a.g;
+#pragma unroll 4
+  for (int c = tid; c < n_chunks; c += 256) {
+    const int row = c >> 5, part = c & 31;
+    const int tf = (int)(((float)row + 0.5f) * inv_g), hf = row - tf * a.g;
+    if (tok_base + tf < L) {
+      const lds_u8* src = lds + (hf * a.bm_tok + tf) * kORow + 32 * part;
+      const f32x4 y0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src);
+      const f32x4 y1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src + 16);
+      float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      const int64_t grow = (int64_t)(seq0 + tok_base + tf) * a.Hq + u * a.g + hf;
+      if (a.gate) {  // times sigmoid(gate) at the same dims
+        const u32x4 gr = *reinterpret_cast<const u32x4*>((const uint16_t*)a.gate + grow * a.q_row + 8 * part);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[2 * e] *= __builtin_amdgcn_rcpf(1.0f + __expf(-bf16_lo(gr[e])));
+          y[2 * e + 1] *= __builtin_amdgcn_rcpf(1.0f + __expf(-bf16_hi(gr[e])));
+        }
+      }
+      *reinterpret_cast<u32x4*>((uint16_t*)a.out + grow * kW + 8 * part) =
+          u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    }
   }
 }
 
