@@ -91,7 +91,7 @@ __device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* 
                : "memory", "m0");
 }
 
-__global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
+__global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __restrict__ items, int hkv, PrefillArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kStages x (K, V)
   lds_u8* lds = (lds_u8*)(smem);
 
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(PrefillArgs a) {
   // Consecutive workgroups take the KV heads of one work item, so each XCD
   // (workgroups are dealt round-robin over the 8 XCDs) keeps to its own heads
   // and their K/V stay in its L2.
-  const int u = blockIdx.x % a.Hkv;
-  const PrefillItem item = a.items[blockIdx.x / a.Hkv];
+  const int u = blockIdx.x % hkv;
+  const PrefillItem item = items[blockIdx.x / hkv];
   const int s = item.s, qt = item.qt;
   const int seq0 = item.seq0;
   const int L = item.len;
@@ -693,7 +693,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int n_items, hipStream_t st
       hipFuncSetAttribute((const void*)k_prefill_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillSmemMax);
   if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), prefill_smem_bytes(a.bm_tok), st, a);
+  hipLaunchKernelGGL(k_prefill_bf16, dim3((unsigned)blocks), dim3(256), prefill_smem_bytes(a.bm_tok), st,
+                     (const PrefillItem*)a.items, a.Hkv, a);
   return hipGetLastError();
 }
 
