@@ -31,11 +31,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
 # Per-source extra flags.  The attention kernels keep their MFMA accumulators
 # in arch VGPRs: the softmax reads every score, and the online softmax rescales
 # every output accumulator, with VALU; the AGPR form made the compiler shuttle
-# them between register files.  The prefill kernel takes its work-item list
+# them between register files.  The prefill kernels take their work-item list
 # and KV-head count as leading scalar arguments, which the wave finds preloaded
 # in SGPRs (kernarg preload), so its first dependent load can issue at once.
 SOURCE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=3"],
-                "k_prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "k_prefill_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=3"],
                 "k_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

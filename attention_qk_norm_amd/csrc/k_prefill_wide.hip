@@ -148,7 +148,7 @@ __device__ __forceinline__ void q_prologue(const PrefillArgs& a, const u32x4 (&r
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
+__global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __restrict__ items, int hkv, PrefillArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kStages x (K, V)
   lds_u8* lds = (lds_u8*)(smem);
 
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(PrefillArgs a) {
   const int lane = tid & 63, w = tid >> 6;
   // Consecutive workgroups take the KV heads of one work item (the XCD
   // round-robin then keeps each XCD on its own heads' K/V in its L2).
-  const int u = blockIdx.x % a.Hkv;
-  const PrefillItem item = a.items[blockIdx.x / a.Hkv];
+  const int u = blockIdx.x % hkv;
+  const PrefillItem item = items[blockIdx.x / hkv];
   const int s = item.s, qt = item.qt, seq0 = item.seq0, L = item.len, p0 = item.p0;
   const int tok_base = qt * a.bm_tok;
   if ((s < 0) | (s >= a.n_seq) | (qt < 0) | (tok_base >= L) | (p0 < 0)) return;
@@ -484,7 +484,7 @@ hipError_t launch_prefill_wide(const PrefillArgs& a, int n_items, hipStream_t st
       hipFuncSetAttribute((const void*)k_prefill_wide, hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
   if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)n_items * a.Hkv;
-  hipLaunchKernelGGL(k_prefill_wide, dim3((unsigned)blocks), dim3(256), kSmem, st, a);
+  hipLaunchKernelGGL(k_prefill_wide, dim3((unsigned)blocks), dim3(256), kSmem, st, (const PrefillItem*)a.items, a.Hkv, a);
   return hipGetLastError();
 }
 
