@@ -431,7 +431,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention core shards by KV head or sequence with no "
-              "exchange, and multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "exchange between GPUs, so one GPU's share at its real shape is what is timed (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
