@@ -65,12 +65,24 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int elem_bytes(qwattn_dtype dt) { return dt == QWATTN_BF16 ? 2 : 4; }
 
+// The tile copies address the rows of one K/V tile (64 rows in prefill, 32 in
+// decode; 256 rows of an operand panel in the projections) from a scalar base
+// with 32-bit per-lane byte offsets, row * row stride + column, so 64 row
+// strides (256 for the projections) must fit in 32 bits.
+constexpr int64_t kMaxTileRowBytes = (int64_t(1) << 32) / 64;  // 64 MiB per K/V row
+constexpr int64_t kMaxGemmRowElems = (int64_t(1) << 32) / 256 / 2;  // bf16 operand row of a projection
+// Bounds that keep every element offset and size product far inside int64.
+constexpr int32_t kMaxHeads = 32768;
+constexpr int64_t kMaxCacheElems = int64_t(1) << 56;
+
 qwattn_status check_params(const qwattn_params* p, qwattn_dtype dt) {
   if (!p) return fail(QWATTN_ERR_INVALID_ARG, "params is NULL");
   if (dt != QWATTN_F32 && dt != QWATTN_BF16) return fail(QWATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   if (p->n_q_heads <= 0 || p->n_kv_heads <= 0)
     return fail(QWATTN_ERR_INVALID_ARG, "head counts must be positive (n_q_heads=%d, n_kv_heads=%d)",
                 p->n_q_heads, p->n_kv_heads);
+  if (p->n_q_heads > kMaxHeads)
+    return fail(QWATTN_ERR_UNSUPPORTED, "n_q_heads=%d > %d", p->n_q_heads, kMaxHeads);
   if (p->n_q_heads % p->n_kv_heads != 0)
     return fail(QWATTN_ERR_INVALID_ARG, "n_q_heads=%d is not a multiple of n_kv_heads=%d", p->n_q_heads,
                 p->n_kv_heads);
@@ -104,18 +116,30 @@ qwattn_status check_ptr(const void* p, const char* name, uintptr_t align = 16) {
   return QWATTN_OK;
 }
 
+// A cache of n_seq sequences x n_kv heads x capacity slots.
 qwattn_status check_cache(const qwattn_cache_desc* c, const void* kc, const void* vc, qwattn_dtype dt,
-                          int head_dim) {
+                          int head_dim, int n_seq, int n_kv) {
   qwattn_status st;
   if ((st = check_ptr(kc, "k_cache")) || (st = check_ptr(vc, "v_cache"))) return st;
   if (!c) return fail(QWATTN_ERR_INVALID_ARG, "cache descriptor is NULL");
   if (c->capacity <= 0) return fail(QWATTN_ERR_INVALID_ARG, "cache capacity must be positive");
   if (c->stride_seq <= 0 || c->stride_head <= 0 || c->stride_tok <= 0)
     return fail(QWATTN_ERR_INVALID_ARG, "cache strides must be positive");
+  if (c->stride_seq > kMaxCacheElems || c->stride_head > kMaxCacheElems || c->stride_tok > kMaxCacheElems)
+    return fail(QWATTN_ERR_INVALID_ARG, "cache stride beyond 2^56 elements");
   const int64_t es = elem_bytes(dt);
   if ((c->stride_seq * es) % 16 || (c->stride_head * es) % 16 || (c->stride_tok * es) % 16)
     return fail(QWATTN_ERR_INVALID_ARG, "cache strides must keep rows 16-byte aligned");
   if (c->stride_tok < head_dim) return fail(QWATTN_ERR_INVALID_ARG, "cache stride_tok < head_dim");
+  if (c->stride_tok * es > kMaxTileRowBytes)
+    return fail(QWATTN_ERR_UNSUPPORTED,
+                "cache stride_tok of %lld bytes > %lld: the kernels address a tile's 64 rows with 32-bit offsets",
+                (long long)(c->stride_tok * es), (long long)kMaxTileRowBytes);
+  // Offset of the last element the call may touch, exactly (128-bit).
+  const __int128 last = (__int128)(n_seq > 0 ? n_seq - 1 : 0) * c->stride_seq +
+                        (__int128)(n_kv > 0 ? n_kv - 1 : 0) * c->stride_head +
+                        (__int128)(c->capacity - 1) * c->stride_tok + head_dim;
+  if (last > kMaxCacheElems) return fail(QWATTN_ERR_INVALID_ARG, "cache extent beyond 2^56 elements");
   return QWATTN_OK;
 }
 
@@ -195,11 +219,25 @@ struct DecodeLayout {
   size_t off_qhat = 0, off_chunk = 0, off_chunk_seq = 0, off_part = 0, total = 0;
 };
 
+// Chunks a call with n_seq sequences and total_keys keys may need: at least
+// sum_i ceil(keys_i / chunk) <= total_keys / chunk + n_seq for its own chunk,
+// and no fewer than a call with fewer keys could need, so that a workspace
+// sized for some total serves every smaller total.  A smaller total can pick
+// a smaller chunk: chunk c < 2048 is picked only while
+// (total / 2c) * n_kv < 2048, i.e. for totals below 2c * ceil(2048 / n_kv),
+// where it makes fewer than 2 * ceil(2048 / n_kv) chunks (+ n_seq).
+int64_t decode_max_chunks(int64_t total_keys, int n_seq, int n_kv) {
+  const int chunk = decode_chunk(total_keys, n_kv);
+  int64_t most = total_keys / chunk;
+  if (chunk > qw::kDecodeKeysPerPass) most = std::max<int64_t>(most, 2 * ((2048 + n_kv - 1) / n_kv));
+  return most + n_seq;
+}
+
 DecodeLayout decode_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, int64_t total_start_pos) {
   DecodeLayout d;
   const int64_t total_keys = total_start_pos + n_seq;
   d.chunk = decode_chunk(total_keys, p->n_kv_heads);
-  d.max_chunks = total_keys / d.chunk + n_seq;  // >= sum_i ceil(keys_i / chunk)
+  d.max_chunks = decode_max_chunks(total_keys, n_seq, p->n_kv_heads);
   size_t off = 0;
   d.off_qhat = off;
   off = align256(off + (size_t)n_seq * p->n_q_heads * p->head_dim * elem_bytes(dt));
@@ -325,7 +363,7 @@ qwattn_status check_sequences(const qwattn_params* params, qwattn_dtype dtype, c
     if (!sp.any_cache) return fail(QWATTN_ERR_INVALID_ARG, "an append needs the KV cache");
   }
   if (sp.any_cache) {
-    if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim))) return st;
+    if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim, n_seq, params->n_kv_heads))) return st;
     for (int s = 0; s < n_seq; ++s) {
       const int64_t p0 = sp.append ? start_pos_host[s] : 0;
       const int64_t L = cu_seqlens_host[s + 1] - cu_seqlens_host[s];
@@ -525,6 +563,17 @@ LayerPlan layer_layout(const qwattn_params* p, int n_seq, int64_t n_tok, int max
   return lp;
 }
 
+// A GEMM's operand rows must keep 256 rows' offsets within 32 bits (see
+// kMaxGemmRowElems), and its tile grid within one launch.
+qwattn_status check_gemm_shape(int64_t m, int64_t n, int64_t k) {
+  if (k > kMaxGemmRowElems)
+    return fail(QWATTN_ERR_UNSUPPORTED, "inner dimension %lld > %lld: operand panels use 32-bit row offsets",
+                (long long)k, (long long)kMaxGemmRowElems);
+  if (m > 0x7fffffffLL || ((m + 255) / 256) * ((n + 255) / 256) > 0x7fffffffLL)
+    return fail(QWATTN_ERR_UNSUPPORTED, "GEMM of %lld x %lld has too many tiles", (long long)m, (long long)n);
+  return QWATTN_OK;
+}
+
 qwattn_status check_layer_params(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden) {
   qwattn_status st;
   if ((st = check_params(params, dtype))) return st;
@@ -534,7 +583,8 @@ qwattn_status check_layer_params(const qwattn_params* params, qwattn_dtype dtype
   if (hidden <= 0 || hidden % 128)
     return fail(hidden <= 0 ? QWATTN_ERR_INVALID_ARG : QWATTN_ERR_UNSUPPORTED,
                 "hidden=%d must be a positive multiple of 128", hidden);
-  return QWATTN_OK;
+  // the q/k/v projection reads rows of hidden values, o_proj rows of Hq * 128
+  return check_gemm_shape(0, 0, std::max<int64_t>(hidden, (int64_t)params->n_q_heads * params->head_dim));
 }
 
 // y = x W^T launch (plain epilogue).
@@ -605,7 +655,7 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
       (st = check_ptr(start_pos, "start_pos", 4)))
     return st;
   if (!start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos_host is NULL");
-  if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim))) return st;
+  if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim, n_seq, params->n_kv_heads))) return st;
   int64_t total = 0;
   for (int i = 0; i < n_seq; ++i) {
     const int sp = start_pos_host[i];
@@ -744,6 +794,7 @@ qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, in
   if (m < 0 || n <= 0 || k <= 0) return fail(QWATTN_ERR_INVALID_ARG, "m >= 0, n > 0 and k > 0 are required");
   if (n % 128 || k % 64)
     return fail(QWATTN_ERR_UNSUPPORTED, "n=%d must be a multiple of 128 and k=%d of 64", n, k);
+  if ((st = check_gemm_shape(m, n, k))) return st;
   if ((st = check_ptr(x, "x")) || (st = check_ptr(w, "w")) || (st = check_ptr(y, "y"))) return st;
   if (m == 0) return QWATTN_OK;
   hipStream_t strm = (hipStream_t)stream;
@@ -779,6 +830,9 @@ qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype d
       (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(y, "y")))
     return st;
   if (sp.n_tok == 0) return QWATTN_OK;
+  if ((st = check_gemm_shape(sp.n_tok, (int64_t)(params->n_q_heads + 2 * params->n_kv_heads) * params->head_dim,
+                             hidden)))
+    return st;
   const LayerPlan lp = layer_layout(params, n_seq, sp.n_tok, sp.max_tiles, sp.n_items, sp.any_cache);
   if ((st = check_workspace(workspace, workspace_bytes, lp.total))) return st;
 

@@ -79,10 +79,18 @@ typedef enum {
   QWATTN_ERR_HIP = 5           /* a HIP runtime call or launch failed             */
 } qwattn_status;
 
-typedef enum { QWATTN_F32 = 0, QWATTN_BF16 = 1 } qwattn_dtype;
+typedef enum {
+  QWATTN_F32 = 0,
+  QWATTN_BF16 = 1,
+  /* Not dtypes: they give the enum the range of int32, so that any value a
+   * caller passes is a valid qwattn_dtype inside the (C++) library and is
+   * rejected with QWATTN_ERR_INVALID_ARG rather than being undefined. */
+  QWATTN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  QWATTN_DTYPE_RANGE_MAX_ = 2147483647
+} qwattn_dtype;
 
 typedef struct {
-  int32_t n_q_heads;    /* query heads, > 0                                        */
+  int32_t n_q_heads;    /* query heads, > 0 and <= 32768                           */
   int32_t n_kv_heads;   /* KV heads, > 0, divides n_q_heads; g = n_q / n_kv <= 128,
                            and <= 16 for a bf16 decode                            */
   int32_t head_dim;     /* 128, or 256 for the gated layers                        */
@@ -101,7 +109,11 @@ typedef struct {
 /* A KV cache: element (seq s, kv head h, slot j, dim d) of k_cache / v_cache is at
  * base + s*stride_seq + h*stride_head + j*stride_tok + d (strides in elements;
  * dim innermost and contiguous; stride_tok * elem_size and every other stride
- * must keep rows 16-byte aligned).  Slots 0 .. capacity-1 exist per sequence. */
+ * must keep rows 16-byte aligned).  Slots 0 .. capacity-1 exist per sequence.
+ * stride_tok * elem_size may be at most 64 MiB (QWATTN_ERR_UNSUPPORTED beyond:
+ * the kernels address the rows of a 64-slot tile with 32-bit byte offsets), and
+ * the last element a call can reach must lie within 2^56 elements of the base
+ * (QWATTN_ERR_INVALID_ARG). */
 typedef struct {
   int64_t stride_seq;
   int64_t stride_head;
@@ -205,7 +217,8 @@ qwattn_status qwattn_append(const qwattn_params* params, qwattn_dtype dtype,
  * nn.Linear without bias; "7.2 Qwen3 全规模实现" §7.2.1 listing].
  *   x [m][k], w [n][k] (the weight as stored, out x in), y [m][n] (device, bf16,
  *   row-major, 16-byte aligned).  fp32 accumulation, y rounded to bf16.
- *   n a multiple of 128 and k a multiple of 64 (QWATTN_ERR_UNSUPPORTED else);
+ *   n a multiple of 128 and k a multiple of 64, k <= 8388608 (operand panels
+ *   use 32-bit row offsets), m <= 2^31 - 1 (QWATTN_ERR_UNSUPPORTED else);
  *   m == 0 is a no-op.  Only QWATTN_BF16. */
 qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, int64_t m, int32_t n, int32_t k,
                             void* y, void* stream);
@@ -215,7 +228,8 @@ qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, in
  * attention, o_proj ["Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE
  * -> attention -> o_proj; "7.2 Qwen3 全规模实现" §7.2.1 listing: heads
  * concatenated in order before out_proj].
- *   hidden: model width (a multiple of 128); x [n_tok][hidden] (device): the
+ *   hidden: model width (a multiple of 128, <= 8388608, as is n_q_heads * 128:
+ *     the projections' inner dimensions); x [n_tok][hidden] (device): the
  *     layer input rows, packed as for qwattn_prefill.
  *   w_qkv [(n_q_heads + 2 n_kv_heads) * 128][hidden] (device): the q_proj, k_proj
  *     and v_proj weights (each stored [out][in]) stacked in that order; head h of
@@ -259,7 +273,9 @@ size_t qwattn_prefill_workspace_size(const qwattn_params* params, qwattn_dtype d
                                      int32_t with_cache);
 
 /* Workspace bytes qwattn_decode needs for n_seq sequences whose start positions
- * sum to total_start_pos (0 on invalid params). */
+ * sum to total_start_pos (0 on invalid params).  Non-decreasing in both: a
+ * workspace sized for (n_seq, T) serves every call with n_seq sequences whose
+ * start positions sum to T or less. */
 size_t qwattn_decode_workspace_size(const qwattn_params* params, qwattn_dtype dtype,
                                     int32_t n_seq, int64_t total_start_pos);
 

@@ -201,3 +201,71 @@ def test_probe_validation(lib):
     assert lib.qwattn_hbm_read_probe(None, 1 << 20, F, None) == B.ERR_INVALID_ARG
     assert lib.qwattn_hbm_read_probe(ODD, 1 << 20, F, None) == B.ERR_INVALID_ARG
     assert lib.qwattn_hbm_read_probe(F, 1 << 20, None, None) == B.ERR_INVALID_ARG
+
+
+def test_cache_row_stride_beyond_32bit_tile_offsets(lib):
+    """A cache whose token stride would overflow the kernels' 32-bit row offsets
+    inside a 64-slot tile is rejected (not silently wrapped), for prefill,
+    append and decode; the largest accepted stride passes that check."""
+    p = B.make_params(32, 8)
+    big = (1 << 26) // 2 + 64  # bf16 elements: one slot row > 64 MiB
+    for stride_tok, status in ((big, B.ERR_UNSUPPORTED), ((1 << 26) // 2, B.ERR_WORKSPACE)):
+        d = B.CacheDesc(stride_tok * 8 * 2, stride_tok * 2, stride_tok, 2)
+        assert prefill(lib, p, cu(0, 2), 1, cache=(F, F, d), ws_bytes=16) == status
+        if status == B.ERR_UNSUPPORTED:
+            assert b"32-bit" in lib.qwattn_last_error()
+        assert append(lib, p, cu(0), cu(0, 2), 1, (F, F, d), ws_bytes=16) == status
+        r = lib.qwattn_decode(ctypes.byref(p), 1, F, F, F, F, F, F, F, ctypes.byref(d), F, cu(1), 1, F, F, 16, None)
+        assert r == status
+    # fp32 rows are 4 bytes per element: half the element stride hits the same limit
+    d = B.CacheDesc(big * 8, big // 2 + 32, big // 2 + 32, 2)
+    assert prefill(lib, p, cu(0, 2), 1, cache=(F, F, d), dtype=0) == B.ERR_UNSUPPORTED
+
+
+def test_cache_extent_and_head_bounds(lib):
+    """Strides or extents past 2^56 elements (which would overflow 64-bit
+    offsets further on) and head counts past 32768 are rejected."""
+    p = B.make_params(32, 8)
+    d = B.CacheDesc(1 << 60, 128, 128, 2)
+    assert prefill(lib, p, cu(0, 2), 1, cache=(F, F, d)) == B.ERR_INVALID_ARG
+    d = B.CacheDesc(1 << 54, 128, 128, 2)                 # 4 x 2^54 + ... > 2^56
+    assert prefill(lib, p, cu(0, 1, 1, 1, 1, 2), 5, cache=(F, F, d)) == B.ERR_INVALID_ARG
+    assert b"extent" in lib.qwattn_last_error()
+    d = B.CacheDesc(1 << 50, 1 << 47, (1 << 25) + 8, 1 << 20)  # extent ~2^50: fine; rows > 64 MiB: not
+    assert prefill(lib, p, cu(0, 2), 1, cache=(F, F, d)) == B.ERR_UNSUPPORTED
+    assert prefill(lib, B.make_params(65536, 65536), cu(0, 2), 1) == B.ERR_UNSUPPORTED
+    assert B.prefill_workspace_size(B.make_params(65536, 8192), B.BF16, 1, 5, 5, False) == 0
+
+
+def test_linear_and_layer_inner_dimension_bounds(lib):
+    """Projections whose inner dimension would overflow the 32-bit panel row
+    offsets, or whose tile grid is too large, are rejected."""
+    f = lib.qwattn_linear
+    assert f(1, F, F, 0, 128, 1 << 23, F, None) == B.OK             # the largest inner dimension (m = 0: no-op)
+    assert f(1, F, F, 16, 128, (1 << 23) + 64, F, None) == B.ERR_UNSUPPORTED
+    assert f(1, F, F, 1 << 31, 128, 64, F, None) == B.ERR_UNSUPPORTED
+    assert f(1, F, F, (1 << 31) - 1, (1 << 31) - 128, 64, F, None) == B.ERR_UNSUPPORTED  # too many tiles
+    p = B.make_params(32, 8)
+    assert B.attention_layer_workspace_size(p, B.BF16, (1 << 23) + 128, 1, 5, 5, False) == 0
+    assert B.attention_layer_workspace_size(p, B.BF16, 4096, 1, 5, 5, False) > 0
+
+
+def test_decode_workspace_size_is_monotone(lib):
+    """A decode workspace sized for a total of start positions serves every
+    smaller total (the chunk length the call picks shrinks with the total, so
+    the bound on the chunk count must not)."""
+    for hkv, hq in ((8, 32), (2, 16), (1, 16), (4, 64)):
+        for dt, d in ((B.BF16, 128), (B.F32, 128), (B.BF16, 256)):
+            p = B.make_params(hq, hkv) if d == 128 else B.make_gated_params(hq, hkv)
+            for n_seq in (1, 7, 64):
+                prev = 0
+                totals = sorted(set([0, 1, 100, 127, 128, 129] + [int(x) for x in
+                                    __import__("numpy").geomspace(1, 1 << 24, 400)] +
+                                    [c * m * ((2048 + hkv - 1) // hkv) + e for c in (128, 256, 512, 1024, 2048)
+                                     for m in (1, 2) for e in (-n_seq - 1, -n_seq, -n_seq + 1, 0)]))
+                for t in totals:
+                    if t < 0:
+                        continue
+                    sz = B.decode_workspace_size(p, dt, n_seq, t)
+                    assert sz >= prev, (hkv, dt, d, n_seq, t, sz, prev)
+                    prev = sz
