@@ -153,13 +153,14 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
+    // The row sum adds the bf16-rounded weights the PV MFMA uses: numerator and
+    // denominator sum the same weights.
     float psum = 0.f;
     bf16x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sv[e] - m_new);
-      psum += p;
-      pf[e] = (__bf16)p;  // virtual key 8 q4 + e
+      pf[e] = (__bf16)__builtin_amdgcn_exp2f(sv[e] - m_new);  // virtual key 8 q4 + e
+      psum += (float)pf[e];
     }
     l_run = l_run * alpha + psum;
 

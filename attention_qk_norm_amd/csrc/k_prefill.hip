@@ -31,14 +31,18 @@
 // log2 units, and |score| <= c * 128 * max|gamma_q| * max|gamma_k| (query rows
 // have norm <= sqrt(128) max|gamma_q|, rotated keys <= sqrt(128) max|gamma_k|,
 // RoPE keeps norms; a small margin covers the bf16 roundings).  When that bound
-// is <= 60, p = 2^score is a normal float for every key (in fp32 and in bf16),
-// so softmax needs no running maximum, no rescaling and no subtraction: the
-// weights are exp2 of the accumulators, and the tile pipelines at 32-key
-// granularity.  Otherwise the kernel runs the usual online softmax.  Both are
-// exactly softmax; only rounding differs.  The row sum adds the bf16-rounded
-// weights the PV MFMA uses, so every output row is an exact convex combination
-// of V rows.  Tiles entirely above a wave's diagonal are skipped; only tiles
-// crossing it are masked.
+// is <= 60, the weights are p = 2^(score - B), B the bound rounded up to an
+// integer: every p lies in [2^-120, 1], a normal float in fp32 and in bf16, so
+// softmax needs no running maximum and no rescaling, and the tile pipelines at
+// 32-key granularity.  The shift costs no instruction: the first score MFMA of
+// a tile takes -B as its accumulator input instead of 0, and the exponential
+// is taken of the accumulator itself.  With p <= 1 the PV accumulators have
+// the range of the online form.  Otherwise the
+// kernel runs the usual online softmax.  Both are exactly softmax; only
+// rounding differs.  The row sum adds the bf16-rounded weights the PV MFMA
+// uses, so every output row is an exact convex combination of V rows.  Tiles
+// entirely above a wave's diagonal are skipped; only tiles crossing it are
+// masked.
 #include <type_traits>
 
 #include "kernels.h"
@@ -183,6 +187,14 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
   // The launch-wide logit bound (decided once by the plan kernel) picks the
   // softmax form.
   const bool use_static = a.static_flag[0] != 0;
+  // Static-bound form: each tile's score accumulators start at -B (B the
+  // launch's logit bound, an integer), so its weights come out as 2^(score - B).
+  f32x16 neg_bound;
+  {
+    const float nb = __int_as_float(a.static_flag[1]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) neg_bound[j] = nb;
+  }
   const float c_log2 = a.scale_log2e;
   // QK-Norm + RoPE of one query row, times c = scale * log2(e) (so the MFMA
   // scores come out in log2 units), into bf16 fragments.  Called once per query
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
     };
     auto smfma = [&](int kb, int kk, int qb) __attribute__((always_inline)) {
       sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[8 * kb + kk], qf[qb][kk],
-                                                             kk == 0 ? f32x16{} : sacc[kb][qb], 0, 0, 0);
+                                                             kk == 0 ? neg_bound : sacc[kb][qb], 0, 0, 0);
     };
     auto pmfma = [&](int i, int qb) __attribute__((always_inline)) {
       o[qb][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[qb][i >> 2], o[qb][i & 3], 0, 0, 0);
@@ -660,8 +672,13 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanArgs a) {
       kmax = fmaxf(kmax, __shfl_xor(kmax, m, 64));
       qmax = fmaxf(qmax, __shfl_xor(qmax, m, 64));
     }
-    if (l == 0)
-      a.static_flag[0] = a.scale_log2e * (float)a.head_dim * qmax * kmax * (1.0f + 1.0f / 64) <= kStaticBoundMax;
+    if (l == 0) {
+      const float bound = a.scale_log2e * (float)a.head_dim * qmax * kmax * (1.0f + 1.0f / 64);
+      const bool ok = bound <= kStaticBoundMax;
+      // the weights are 2^(score - B), B = the bound rounded up: in [2^-120, 1]
+      a.static_flag[0] = ok;
+      a.static_flag[1] = __float_as_int(ok ? -ceilf(bound) : 0.f);
+    }
   }
   for (int s = 0; s < a.n_seq; ++s) {
     const int nt = n_tiles_of(s);

@@ -32,10 +32,10 @@
 //
 // Softmax: as in the head_dim-128 kernel, the query rows are pre-multiplied by
 // c = scale * log2(e); when the launch-wide bound c * 256 * max|scale_q| *
-// max|scale_k| (plus a rounding margin) is <= 60, p = 2^score needs no running
-// maximum (the static-bound form, decided by the plan kernel); otherwise the
-// online softmax runs.  The row sum adds the bf16-rounded weights that the PV
-// MFMA uses.
+// max|scale_k| (plus a rounding margin) is <= 60, p = 2^(score - B), B that
+// bound rounded up, lies in [2^-120, 1] and needs no running maximum (the
+// static-bound form, decided by the plan kernel; the first score MFMA of a
+// tile starts its accumulator at -B); otherwise the online softmax runs.  The row sum adds the bf16-rounded weights that the PV MFMA uses.
 #include <type_traits>
 
 #include "kernels.h"
@@ -222,6 +222,14 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
     default: q_prologue<256>(a, qraw, valid, qp, hg, qf); break;
   }
   const bool use_static = a.static_flag[0] != 0;
+  // Static-bound form: each tile's score accumulators start at -B (B the
+  // launch's logit bound, an integer), so its weights come out as 2^(score - B).
+  f32x16 neg_bound;
+  {
+    const float nb = __int_as_float(a.static_flag[1]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) neg_bound[j] = nb;
+  }
 
   f32x16 o[8];
 #pragma unroll
@@ -249,8 +257,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
+      sacc[kb] = kStatic ? neg_bound : f32x16{};
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
         const bf16x8 ka = lds_load_b128(ks + k_base + kb * 512 + kk * 32);
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
       else if (r < 64) vread(r - 32);
     };
     auto smfma = [&](int kb, int kk) __attribute__((always_inline)) {
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[16 * kb + kk], qf[kk], kk == 0 ? f32x16{} : sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[16 * kb + kk], qf[kk], kk == 0 ? neg_bound : sacc[kb], 0, 0, 0);
     };
     auto pmfma = [&](int i) __attribute__((always_inline)) {
       o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[i >> 3], o[i & 7], 0, 0, 0);

@@ -64,7 +64,9 @@ struct PlanArgs {
   float scale_log2e;
   float gamma_offset;        // norm scale = gamma_offset + gamma
   int head_dim;
-  int32_t* static_flag;      // out: 1 when the static-bound softmax applies
+  int32_t* static_flag;      // out: [0] 1 when the static-bound softmax applies; [1] the
+                             // float -B, B its logit bound rounded up (the weights are
+                             // 2^(score - B))
 };
 hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t st);
 
@@ -85,7 +87,7 @@ struct PrefillArgs {
   const int32_t* start_pos; // decode (fp32 path): position of each sequence's new token;
                             // prefill: NULL, or (an append) position of each sequence's first row
   const PrefillItem* items;
-  const int32_t* static_flag;  // bf16 path: written by the plan kernel
+  const int32_t* static_flag;  // bf16 path: written by the plan kernel ([0] form, [1] shift)
   void* out;
   int n_seq, Hq, Hkv, g, bm_tok;
   int decode;               // fp32 path: items are (seq, 0), one query token at start_pos

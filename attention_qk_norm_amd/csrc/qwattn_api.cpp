@@ -198,7 +198,7 @@ PrefillPlan prefill_layout(const qwattn_params* p, qwattn_dtype dt, int n_seq, i
   pl.off_items = off;
   off = align256(off + (size_t)n_items * sizeof(qw::PrefillItem));
   pl.off_flag = off;
-  off = align256(off + 4);
+  off = align256(off + 8);  // the softmax form and its weight shift
   pl.total = off;
   return pl;
 }

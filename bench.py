@@ -1,20 +1,24 @@
 """Benchmark of the attention-sublayer core on one MI355X.
 
 One step = the whole hot path on synthetic Qwen3-shaped inputs resident in HBM:
-  * qwattn_prefill on the Qwen3-8B-shaped prefill (B=4 x T=4096, Hq=32, Hkv=8,
-    bf16): norm+RoPE of K into a KV cache, the tile plan, and the causal GQA
-    attention kernel with the fused Q norm+RoPE prologue;
+  * qwattn_prefill on the Qwen3-32B-shaped long prefill (B=1 x T=32768, Hq=64,
+    Hkv=8, bf16): norm+RoPE of K into a KV cache, the tile plan, and the causal
+    GQA attention kernel with the fused Q norm+RoPE prologue;
   * qwattn_decode on the Qwen3-8B-shaped decode (64 sequences, contexts
     U[1024, 32768], bf16 cache): the new-token prologue, split-K attention and
     the combine.
-Prints one JSON line.  ``value`` is prefill attention TFLOP/s (algorithmic flops:
-unmasked causal pairs only); the decode KV-read GB/s sits under ``decode``.
-Besides the step, the line carries chunked-prefill (``append``), the gated
-head_dim-256 layer of Qwen3-Next (``gated``: prefill and decode) and the whole
-attention sublayer with its projections (``layer``) figures.
+Prints one JSON line.  ``value`` is prefill attention TFLOP/s of the long
+prefill over the whole call (algorithmic flops: unmasked causal pairs only);
+the decode KV-read GB/s sits under ``decode``.  The other prefill workloads
+(Qwen3-8B 4 x 4096 and the Qwen3-235B-A22B-attention ragged batch) are timed
+after the steps, each with its own roofline, under ``prefill_workloads``.
+The line also carries chunked-prefill (``append``), the gated head_dim-256
+layer of Qwen3-Next (``gated``: prefill and decode) and the whole attention
+sublayer with its projections (``layer``) figures, and the CPU oracle timed on
+bounded samples (``cpu_baseline`` for the long prefill, ``decode.cpu_baseline``).
 
-    python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--no-decode]
-                    [--no-cpu-baseline] [--no-append] [--no-gated] [--no-layer] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--extra-prefill 1,4|none]
+                    [--no-decode] [--no-cpu-baseline] [--no-append] [--no-gated] [--no-layer] [--gpus 1]
 """
 
 import argparse
@@ -31,6 +35,8 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+HEADLINE_PREFILL = 3             # the long prefill: 1 x 32768 tokens, 64 / 8 heads
+EXTRA_PREFILL = "1,4"            # the other prefill workloads, timed beside the steps
 
 
 class HipEvents:
@@ -55,10 +61,10 @@ class HipEvents:
         return ms.value
 
 
-def recorded_traffic(kernel, source):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic_*.md), or None when none was taken for the
-    current kernel source."""
+def recorded_traffic(kernel, source, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summaries (profiles/hbm_traffic_*.md), or None when none
+    was taken for the current kernel source."""
     import glob
     import hashlib
     path = os.path.join(ROOT, "attention_qk_norm_amd", "csrc", source)
@@ -68,10 +74,12 @@ def recorded_traffic(kernel, source):
         if "```json" not in text:
             continue
         block = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-        rec = block.get(kernel)
-        if rec and rec.get("source_sha256_16") == sha:
-            return {"bytes": int(rec["read_bytes"]) + int(rec["write_bytes"]), "read_bytes": int(rec["read_bytes"]),
-                    "write_bytes": int(rec["write_bytes"]), "from": os.path.relpath(f, ROOT)}
+        for rec in block.values():
+            if (rec.get("kernel_id") == kernel and rec.get("workload") == workload and
+                    rec.get("source_sha256_16") == sha):
+                return {"bytes": int(rec["read_bytes"]) + int(rec["write_bytes"]),
+                        "read_bytes": int(rec["read_bytes"]), "write_bytes": int(rec["write_bytes"]),
+                        "from": os.path.relpath(f, ROOT)}
     return None
 
 
@@ -107,6 +115,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def pct(v):
+    """p10 / median / p90 of timed iterations (ms)."""
+    return [round(float(x), 4) for x in np.percentile(v, [10, 50, 90])]
+
+
 def setup_prefill(case_id, dev):
     import torch
     from attention_qk_norm_amd import binding as B, inputs
@@ -115,8 +128,9 @@ def setup_prefill(case_id, dev):
     x = inputs.prefill_inputs(spec)
     bf = torch.bfloat16
     up = lambda a: torch.from_numpy(a).to(dev).to(bf)
-    st = dict(spec=spec, x=x, q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), qg=up(x["q_gamma"]), kg=up(x["k_gamma"]),
+    st = dict(spec=spec, q=up(x["q"]), k=up(x["k"]), v=up(x["v"]), qg=up(x["q_gamma"]), kg=up(x["k_gamma"]),
               cu=torch.from_numpy(x["cu_seqlens"]).to(dev), cu_h=x["cu_seqlens"])
+    del x
     cap = (max(spec.lengths) + 63) // 64 * 64
     st["kc"] = torch.empty(spec.n_seq, spec.n_kv_heads, cap, 128, dtype=bf, device=dev)
     st["vc"] = torch.empty_like(st["kc"])
@@ -132,6 +146,28 @@ def run_prefill(st):
     from attention_qk_norm_amd import binding as B
     B.prefill(st["params"], st["q"], st["k"], st["v"], st["qg"], st["kg"], st["cu"], st["cu_h"], out=st["out"],
               k_cache=st["kc"], v_cache=st["vc"], workspace=st["ws"])
+
+
+def prefill_record(spec, call_all, kern_all, peaks=None):
+    """Throughput of a prefill workload: over the whole call (``value``) and of
+    the attention kernel against the bf16 MFMA peak (``roofline``)."""
+    from attention_qk_norm_amd import accounting
+    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    call_ms, kern_ms = float(np.mean(call_all)), float(np.mean(kern_all))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    roof = {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip", spec.workload),
+            "kernel_ms": round(kern_ms, 4), "kernel_ms_p10_p50_p90": pct(kern_all), "algorithmic_flops": flops}
+    if peaks is not None:
+        roof["measured_peak"] = {"value": peaks["mfma_tflops"], "unit": "TFLOP/s",
+                                 "frac": round(achieved / peaks["mfma_tflops"], 4),
+                                 "how": "register-only v_mfma_f32_32x32x16_bf16 loop, one wave per SIMD on "
+                                        "every CU, this run (qwattn_mfma_probe)"}
+    value = flops / (call_ms * 1e-3) / 1e12
+    return {"metric": "prefill attention TFLOP/s", "unit": "TFLOP/s", "workload": spec.workload,
+            "value": round(value, 2), "call_ms": round(call_ms, 4), "call_ms_p10_p50_p90": pct(call_all),
+            "frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4), "roofline": roof}
 
 
 def setup_decode(case_id, dev):
@@ -172,6 +208,43 @@ def run_decode(st):
     from attention_qk_norm_amd import binding as B
     B.decode(st["params"], st["q"], st["k"], st["v"], st["qg"], st["kg"], st["kc"], st["vc"], st["sp"], st["sp_h"],
              out=st["out"], workspace=st["ws"])
+
+
+def _timed_lists(run, n_calls):
+    """Per-call times (torch events around the call) and dominant-kernel times
+    (the library's timing hook: HIP events on its stream), in ms."""
+    import torch
+    from attention_qk_norm_amd import binding as B
+    ev = HipEvents()
+    kev = [(ev.create(), ev.create()) for _ in range(n_calls)]
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    torch.cuda.synchronize()
+    for (ka, kb), (ca, cb) in zip(kev, cev):
+        B.set_timing_events(ka, kb)
+        ca.record()
+        run()
+        cb.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in cev], [ev.elapsed_ms(a, b) for a, b in kev]
+
+
+def _timed(run, n_calls):
+    """Mean call time and mean dominant-kernel time, in ms."""
+    c, k = _timed_lists(run, n_calls)
+    return float(np.mean(c)), float(np.mean(k))
+
+
+def measure_prefill_workload(case_id, dev, n_calls=10, warmup=2):
+    """One prefill workload on its own: warm-up calls, then n_calls timed."""
+    import torch
+    st = setup_prefill(case_id, dev)
+    for _ in range(warmup):
+        run_prefill(st)
+    c, k = _timed_lists(lambda: run_prefill(st), n_calls)
+    rec = prefill_record(st["spec"], c, k)
+    del st
+    torch.cuda.empty_cache()
+    return rec
 
 
 def measure_append(dev, n_calls=10, new_tokens=512):
@@ -229,25 +302,6 @@ def measure_append(dev, n_calls=10, new_tokens=512):
                          "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
 
 
-def _timed(run, n_calls):
-    """Mean call time (torch events around the call) and mean dominant-kernel
-    time (the library's timing hook, HIP events on its stream), in ms."""
-    import torch
-    from attention_qk_norm_amd import binding as B
-    ev = HipEvents()
-    kev = [(ev.create(), ev.create()) for _ in range(n_calls)]
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    torch.cuda.synchronize()
-    for (ka, kb), (ca, cb) in zip(kev, cev):
-        B.set_timing_events(ka, kb)
-        ca.record()
-        run()
-        cb.record()
-    torch.cuda.synchronize()
-    return (float(np.mean([a.elapsed_time(b) for a, b in cev])),
-            float(np.mean([ev.elapsed_ms(a, b) for a, b in kev])))
-
-
 def measure_gated(dev, n_calls=10):
     """The gated global layer of Qwen3-Next (head_dim 256, 16 query / 2 KV heads,
     rotary 64 of 256, zero-centred norm, sigmoid output gate): prefill of
@@ -283,7 +337,7 @@ def measure_gated(dev, n_calls=10):
         "roofline": {"kernel": "k_prefill_wide", "bound": "mfma", "achieved": round(flops / (k_ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("k_prefill_wide", "k_prefill_wide.hip"),
+                     "traffic": recorded_traffic("k_prefill_wide", "k_prefill_wide.hip", spec.workload),
                      "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
     del q, k, v, kc, vc, out, ws
 
@@ -317,7 +371,8 @@ def measure_gated(dev, n_calls=10):
         "value": round(kv / (c_ms * 1e-3) / 1e9, 1), "call_ms": round(c_ms, 4), "kv_read_bytes": kv,
         "roofline": {"kernel": "k_decode_split", "bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kv / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("k_decode_split_256", "k_decode.hip"), "kernel_ms": round(k_ms, 4)}}
+                     "traffic": recorded_traffic("k_decode_split", "k_decode.hip", spec.workload),
+                     "kernel_ms": round(k_ms, 4)}}
     return res
 
 
@@ -365,9 +420,9 @@ def measure_layer(dev, n_calls=10):
             "workload": spec.workload, "value": round(total / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
             "algorithmic_flops": total,
             "roofline": dict(kernel="k_gemm<qkv> (fused q/k/v projection)", bound="mfma", **gemm(qkv_flops, qkv_ms),
-                             traffic=recorded_traffic("k_gemm_qkv", "k_gemm.hip")),
+                             traffic=recorded_traffic("k_gemm_qkv", "k_gemm.hip", spec.workload)),
             "o_proj": dict(kernel="k_gemm<plain> via qwattn_linear", bound="mfma", **gemm(o_flops, o_ms),
-                           traffic=recorded_traffic("k_gemm_plain", "k_gemm.hip"))}
+                           traffic=recorded_traffic("k_gemm_plain", "k_gemm.hip", spec.workload))}
 
 
 def copy_calibration(dev):
@@ -382,34 +437,85 @@ def copy_calibration(dev):
     return {"read": 1 << 30, "write": 1 << 30}
 
 
-def cpu_baseline_prefill(spec, n_sample=3):
-    """The oracle, as it stands, on a bounded sample of the prefill workload:
-    the first `n_sample` whole sequences of the packed batch (all query heads,
-    every causal row), about 10-15 s of host work."""
-    import oracle
-    from attention_qk_norm_amd import accounting, inputs
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = None
-    n = min(n_sample, spec.n_seq)
+        return None
+
+
+def stratified_rows(L, block, stride, rng):
+    """Query rows of a stratified sample: the rows of each sequence are cut into
+    blocks of `block` rows, the blocks into strata of `stride` consecutive
+    blocks; one block per stratum is drawn, and the last block is always in."""
+    n_blocks = (L + block - 1) // block
+    picks = set()
+    for s0 in range(0, n_blocks, stride):
+        picks.add(int(rng.integers(s0, min(n_blocks, s0 + stride))))
+    picks.add(n_blocks - 1)
+    return np.concatenate([np.arange(b * block, min(L, (b + 1) * block)) for b in sorted(picks)])
+
+
+def cpu_baseline_prefill(spec, stride=16, block=128, seed=0x51A7):
+    """The oracle, as it stands, on a seeded stratified sample of the prefill
+    workload: 1 in `stride` query-row blocks of every sequence (all query
+    heads, the sequence's last block always in), each row by the oracle's
+    definition with every key it sees.  Its time scaled by all causal pairs
+    over the sampled pairs is the extrapolated time of the whole workload."""
+    import oracle
+    from attention_qk_norm_amd import accounting, inputs
+    rng = np.random.default_rng(seed)
     gq, gk = inputs.gammas(spec)
-    dt, flops = 0.0, 0
-    for sq in range(n):
+    dt, pairs = 0.0, 0
+    n_rows = 0
+    for sq in range(spec.n_seq):
         L = spec.lengths[sq]
-        q = inputs.prefill_seq_rows(spec, sq, 0, L, "q")
-        k = inputs.prefill_seq_rows(spec, sq, 0, L, "k")
-        v = inputs.prefill_seq_rows(spec, sq, 0, L, "v")
+        rows = stratified_rows(L, block, stride, rng)
+        starts = sorted(set(int(r) // block * block for r in rows))
+        q = np.concatenate([inputs.prefill_seq_rows(spec, sq, a, min(L, a + block), "q") for a in starts])
+        k = inputs.prefill_seq_rows(spec, sq, 0, int(rows.max()) + 1, "k")
+        v = inputs.prefill_seq_rows(spec, sq, 0, int(rows.max()) + 1, "v")
         t0 = time.perf_counter()
-        oracle.attention_prefill(q, k, v, gq, gk, [0, L], spec.n_q_heads, spec.n_kv_heads,
-                                 eps=spec.eps, theta=spec.theta)
+        oracle.attention_prefill_rows(q, k, v, gq, gk, rows, np.arange(spec.n_q_heads), spec.n_q_heads,
+                                      spec.n_kv_heads, eps=spec.eps, theta=spec.theta)
         dt += time.perf_counter() - t0
-        flops += accounting.prefill_flops([L], spec.n_q_heads)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(), "blas_threads": blas_threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"the first {n} sequences of the batch ({n} x {spec.lengths[0]} tokens, all "
-                      f"{spec.n_q_heads} query heads): numpy float64 oracle, algorithmic causal flops"}
+        pairs += int((rows + 1).sum())
+        n_rows += len(rows)
+    total_pairs = accounting.prefill_pairs(spec.lengths)
+    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    full_s = dt * total_pairs / pairs
+    return {"value": flops / full_s / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(), "blas_threads": _blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 2), "extrapolated_seconds": round(full_s, 1),
+            "sample": f"{spec.workload}: seeded stratified sample of 1 in {stride} query-row blocks of {block} rows "
+                      f"per sequence (the last block always in), {n_rows} rows x all {spec.n_q_heads} query heads "
+                      f"({pairs / total_pairs:.4f} of the causal pairs), each row with every key it sees; numpy "
+                      "float64 oracle; time extrapolated by causal pairs (labelled: extrapolated)"}
+
+
+def cpu_baseline_decode(spec, n_sample=8, seed=0x51A7):
+    """The oracle's decode on a seeded sample of the batch's sequences (their
+    caches' keys normed and rotated by the oracle beforehand, untimed: a cache
+    holds them so), in KV-read GB/s over the sampled sequences' cache bytes."""
+    import oracle
+    from attention_qk_norm_amd import accounting, inputs
+    rng = np.random.default_rng(seed)
+    seqs = sorted(rng.choice(spec.n_seq, size=min(n_sample, spec.n_seq), replace=False).tolist())
+    x = inputs.decode_new_token(spec)
+    raws = inputs.decode_cache_raw_all(spec, seqs)
+    dt = 0.0
+    for i, (kr, vr) in zip(seqs, raws):
+        L = spec.lengths[i]
+        kh = oracle.qk_norm_rope(kr, x["k_gamma"], np.arange(L), spec.eps, spec.theta)
+        t0 = time.perf_counter()
+        oracle.attention_decode(x["q"][i:i + 1], x["k"][i:i + 1], x["v"][i:i + 1], x["q_gamma"], x["k_gamma"],
+                                [kh], [vr], [L], spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, theta=spec.theta)
+        dt += time.perf_counter() - t0
+    kv = accounting.decode_kv_read_bytes([spec.lengths[i] for i in seqs], spec.n_kv_heads)
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": os.cpu_count(), "blas_threads": _blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{spec.workload}: {len(seqs)} seeded sequences of the 64 ({sum(spec.lengths[i] for i in seqs)} "
+                      "cached tokens), one decode step each; numpy float64 oracle, KV bytes read over its time"}
 
 
 def main():
@@ -417,7 +523,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--prefill-case", type=int, default=1, choices=[1, 3, 4])
+    ap.add_argument("--prefill-case", type=int, default=HEADLINE_PREFILL, choices=[1, 3, 4],
+                    help="the prefill workload of the step (default: the long prefill)")
+    ap.add_argument("--extra-prefill", default=EXTRA_PREFILL,
+                    help="comma-separated prefill workloads timed beside the steps, or 'none'")
     ap.add_argument("--decode-case", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -433,6 +542,8 @@ def main():
         print("bench.py measures one GPU only: the attention core shards by KV head or sequence with no "
               "exchange between GPUs, so one GPU's share at its real shape is what is timed (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    extra = [] if args.extra_prefill in ("", "none") else [int(c) for c in args.extra_prefill.split(",")]
+    extra = [c for c in extra if c != args.prefill_case]
 
     import torch
     from attention_qk_norm_amd import accounting, binding as B
@@ -484,38 +595,21 @@ def main():
     peaks = measure_peaks(dev, dec["kc"] if dec is not None else torch.ones(1 << 29, dtype=torch.int32, device=dev))
 
     spec = pre["spec"]
-    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
-    attn_all = [ev.elapsed_ms(a, b) for a, b in pre_ev]
-    pre_call_all = [e[0].elapsed_time(e[1]) for e in call_ev]
-    attn_ms = float(np.mean(attn_all))
-    pre_call_ms = float(np.mean(pre_call_all))
-
-    def pct(v):  # p10 / median / p90 of the timed iterations, ms
-        return [round(float(x), 4) for x in np.percentile(v, [10, 50, 90])]
-    value = flops / (pre_call_ms * 1e-3) / 1e12
-    achieved = flops / (attn_ms * 1e-3) / 1e12
+    headline = prefill_record(spec, [e[0].elapsed_time(e[1]) for e in call_ev],
+                              [ev.elapsed_ms(a, b) for a, b in pre_ev], peaks)
     rec = {
         "metric": "prefill attention TFLOP/s (causal GQA with fused QK-Norm+RoPE)",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "value": headline["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
         "ms_per_step": round(wall / n * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.workload, "global_batch": spec.n_seq, "seq_len": max(spec.lengths),
                    "n_q_heads": spec.n_q_heads, "n_kv_heads": spec.n_kv_heads, "head_dim": 128,
                    "rope_theta": spec.theta, "parallelism": "single-gpu",
                    "decode_workload": None if dec is None else dec["spec"].workload},
-        "prefill_call_ms": round(pre_call_ms, 4),
-        "prefill_call_ms_p10_p50_p90": pct(pre_call_all),
-        "prefill_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip") if args.prefill_case == 1 else None,
-                     "kernel_ms": round(attn_ms, 4), "kernel_ms_p10_p50_p90": pct(attn_all),
-                     "algorithmic_flops": flops,
-                     "measured_peak": {"value": peaks["mfma_tflops"], "unit": "TFLOP/s",
-                                       "frac": round(achieved / peaks["mfma_tflops"], 4),
-                                       "how": "register-only v_mfma_f32_32x32x16_bf16 loop, one wave per SIMD on "
-                                              "every CU, this run (qwattn_mfma_probe)"}},
+        "prefill_call_ms": headline["call_ms"],
+        "prefill_call_ms_p10_p50_p90": headline["call_ms_p10_p50_p90"],
+        "prefill_frac_mfma_peak": headline["frac_mfma_peak"],
+        "roofline": headline["roofline"],
     }
     if dec is not None:
         ds = dec["spec"]
@@ -533,17 +627,23 @@ def main():
             "roofline": {"kernel": "k_decode_split", "bound": "hbm",
                          "achieved": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": recorded_traffic("k_decode_split", "k_decode.hip") if args.decode_case == 2 else None,
+                         "traffic": recorded_traffic("k_decode_split", "k_decode.hip", ds.workload),
                          "kernel_ms": round(split_ms, 4), "kernel_ms_p10_p50_p90": pct(split_all),
                          "measured_peak": {"value": peaks["hbm_read_gbs"], "unit": "GB/s",
                                            "frac": round(kv_bytes / (split_ms * 1e-3) / 1e9 / peaks["hbm_read_gbs"], 4),
                                            "how": f"one nontemporal streaming read of {peaks['hbm_read_bytes']} bytes "
                                                   "(the K cache), this run (qwattn_hbm_read_probe)"}},
         }
+    del pre, dec
+    torch.cuda.empty_cache()
+    if extra:
+        rec["prefill_workloads"] = {}
+        for c in extra:
+            log(f"prefill workload {c}")
+            rec["prefill_workloads"][str(c)] = measure_prefill_workload(c, dev)
     if not args.no_append:
         log("append (chunked prefill) measurement")
         rec["append"] = measure_append(dev)
-    del pre, dec
     if not args.no_gated:
         torch.cuda.empty_cache()
         log("gated-layer measurements")
@@ -555,8 +655,12 @@ def main():
     if args.copy_calibration:
         rec["copy_calibration_bytes"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample")
+        log("timing the CPU oracle on a stratified sample of the prefill workload")
         rec["cpu_baseline"] = cpu_baseline_prefill(spec)
+        if "decode" in rec:
+            from attention_qk_norm_amd import inputs
+            log("timing the CPU oracle on a sample of the decode workload")
+            rec["decode"]["cpu_baseline"] = cpu_baseline_decode(inputs.case_spec(args.decode_case))
     print(json.dumps(rec), flush=True)
 
 

@@ -64,7 +64,7 @@ hipError_t launch_prefill_plan(const PlanArgs& a, hipStream_t) {
   ++stub::launches;
   stub::write(a.scratch, (4 * ((int64_t)a.max_tiles + 1) + a.n_seq) * sizeof(int32_t));
   stub::write(a.items, (size_t)a.n_items * sizeof(PrefillItem));
-  if (a.static_flag) stub::write(a.static_flag, sizeof(int32_t));
+  if (a.static_flag) stub::write(a.static_flag, 2 * sizeof(int32_t));
   return hipSuccess;
 }
 
@@ -72,7 +72,7 @@ static hipError_t attention(const PrefillArgs& a, int n_items, bool bf16) {
   ++stub::launches;
   const size_t es = bf16 ? 2 : 4;
   stub::read(a.items, (size_t)n_items * sizeof(PrefillItem));
-  if (a.static_flag) stub::read(a.static_flag, sizeof(int32_t));
+  if (a.static_flag) stub::read(a.static_flag, 2 * sizeof(int32_t));
   if (!bf16) stub::read(a.qhat, stub::n_tok * a.Hq * a.head_dim * 4);
   if (a.k_packed) stub::read(a.khat, stub::n_tok * a.Hkv * a.head_dim * es);
   if (a.v_packed) stub::read(a.v, stub::n_tok * a.Hkv * a.head_dim * es);

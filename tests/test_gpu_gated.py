@@ -111,6 +111,29 @@ def run_gated_prefill(cid, dtype, hq, hkv, lengths, rot):
     check(U.down(out), ref, spec, f"gated prefill {cid}")
 
 
+def test_gated_prefill_large_magnitude_v():
+    """V times 2^118 on the head_dim-256 kernel's static-bound path: its weights
+    2^(score - B) are <= 1, so the fp32 accumulators stay finite.  The output
+    divided by 2^118 meets the literal bounds (the gate scales by at most 1)."""
+    spec = inputs.gated_spec(179, "bf16", 16, 2, [1, 65, 200, 517], rot=64, v_scaled=False)
+    x = dict(inputs.prefill_inputs(spec))
+    big = 2.0 ** 118
+    x["v"] = (x["v"] * np.float32(big)).astype(np.float32)
+    U.say("gated prefill, large-magnitude V")
+    dt = torch.bfloat16
+    cu = torch.from_numpy(x["cu_seqlens"]).to(U.DEV)
+    out = B.prefill(gparams(spec), U.up(q_proj(x), dt), U.up(x["k"], dt), U.up(x["v"], dt),
+                    U.up(x["q_gamma"], dt), U.up(x["k_gamma"], dt), cu, x["cu_seqlens"])
+    torch.cuda.synchronize()
+    ref = oracle.gated_attention_prefill(x["q"], x["gate"], x["k"], x["v"], x["q_gamma"], x["k_gamma"],
+                                         x["cu_seqlens"], 16, 2, eps=spec.eps, theta=spec.theta, rot_dim=64)
+    got = U.down(out)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref) / big
+    print(f"gated large V: max {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_head_dim_256_without_gate(dtype):
     """output_gate = 0: the plain attention of the head_dim-256 layer (the

@@ -105,9 +105,16 @@ def test_attention_layer_small(cid, hq, hkv, lengths, hidden, with_cache):
             L = b - a
             kh = oracle.qk_norm_rope(kref[a:b].reshape(L, hkv, 128), gk, np.arange(L), spec.eps, spec.theta)
             got_k = U.down(kc[s, :, :L].permute(1, 0, 2))
-            # the projection bound, scaled by the norm's 1/rms and the scale, plus one bf16 rounding
-            rms = np.sqrt(np.mean(kref[a:b].reshape(L, hkv, 128) ** 2, axis=-1, keepdims=True) + spec.eps)
-            kbound = kb[a:b].reshape(L, hkv, 128).max(axis=-1, keepdims=True) / rms * np.abs(gk).max() * 4 \
+            # First-order propagation of the projection error e (|e_i| <= eps_i) through
+            # the norm and the rotation.  k/r(k), r = sqrt(mean k^2 + eps), moves by
+            # e_i/r - k_i (k.e)/(d r^3), and |k.e| <= |k| |e| <= sqrt(d) r sqrt(d) max eps,
+            # so each coordinate moves by at most (max eps / r)(1 + max_i |k_i| / r);
+            # the rotation adds two coordinates (|cos| + |sin| <= 2 with gamma),
+            # and the result is rounded once to bf16 (2^-9 |k|, doubled for slack).
+            kr3 = kref[a:b].reshape(L, hkv, 128)
+            rms = np.sqrt(np.mean(kr3 ** 2, axis=-1, keepdims=True) + spec.eps)
+            emax = kb[a:b].reshape(L, hkv, 128).max(axis=-1, keepdims=True)
+            kbound = 2.0 * np.abs(gk).max() * (emax / rms) * (1.0 + np.abs(kr3).max(axis=-1, keepdims=True) / rms) \
                 + 2.0 ** -8 * np.abs(kh) + 1e-6
             assert np.all(np.abs(got_k - kh) <= kbound), np.abs(got_k - kh).max()
             got_v = U.down(vc[s, :, :L].permute(1, 0, 2))

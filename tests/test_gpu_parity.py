@@ -223,6 +223,45 @@ def test_prefill_online_softmax_path():
             assert torch.equal(out_t[cu[s], t], U.up(x["v"][cu[s], t // 4], torch.bfloat16))
 
 
+V_BIG = 2.0 ** 118
+
+
+@pytest.mark.parametrize("online", [False, True], ids=["static", "online"])
+def test_prefill_large_magnitude_v(online):
+    """V near the top of the bf16 range (v ~ N(0, 1) times 2^118, about 3e35 per
+    unit): the static-bound weights 2^(score - B) and the online weights
+    2^(score - max) are both <= 1, so the fp32 accumulators hold sums of a few
+    hundred weighted v's and stay finite (weights 2^score, up to 2^B with B
+    near 28 here, would overflow them).  Same bounds as every bf16 case, on
+    the output divided by 2^118; the first row of every sequence is v_0
+    exactly.  ``online`` lifts the launch-wide logit bound past 60 with one
+    large gamma entry in q and k, as in the online-path test."""
+    spec = inputs.custom_spec(124, "bf16", 8, 2, [1, 64, 65, 200, 517], v_scaled=False)
+    x = dict(inputs.prefill_inputs(spec))
+    x["v"] = (x["v"] * np.float32(V_BIG)).astype(np.float32)  # exact: a power of two
+    if online:
+        x["q_gamma"] = x["q_gamma"].copy()
+        x["k_gamma"] = x["k_gamma"].copy()
+        x["q_gamma"][5] = 3.5
+        x["k_gamma"][70] = -3.0
+    bound = (1.0 / np.sqrt(128.0)) * np.log2(np.e) * 128.0 * np.abs(x["q_gamma"]).max() * \
+        np.abs(x["k_gamma"]).max() * (1.0 + 1.0 / 64)
+    assert (bound > 60.0) == online, bound
+    U.say(f"prefill large-magnitude V, {'online' if online else 'static-bound'} softmax (bound {bound:.1f})")
+    out_t = U.run_prefill(spec, x)
+    out = U.down(out_t)
+    ref = oracle.attention_prefill(x["q"], x["k"], x["v"], x["q_gamma"], x["k_gamma"], x["cu_seqlens"], 8, 2,
+                                   eps=spec.eps, theta=spec.theta)
+    assert np.isfinite(out).all()
+    err = np.abs(out - ref) / V_BIG
+    print(f"large V ({'online' if online else 'static'}): max {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    cu = x["cu_seqlens"]
+    for s in range(len(spec.lengths)):
+        for t in range(8):
+            assert torch.equal(out_t[cu[s], t], U.up(x["v"][cu[s], t // 4], torch.bfloat16))
+
+
 def test_prefill_many_short_sequences():
     """2100 packed sequences of 0..9 tokens: the plan kernel's large-plan path
     (more sequences than its LDS arrays hold), empty sequences included."""
@@ -237,11 +276,15 @@ def test_prefill_many_short_sequences():
     print(U.bf16_gate(out, ref, spec, label="many short sequences"))
 
 
+@pytest.mark.parametrize("v_scaled", [True, False], ids=["v-scaled", "v-unscaled"])
 @pytest.mark.parametrize("case_id", [1, 3, 4])
-def test_prefill_full_size_sampled(case_id):
+def test_prefill_full_size_sampled(case_id, v_scaled):
     """Full-size standard workloads in the benchmark's launch configuration;
-    seeded row samples of every sequence checked against the oracle."""
-    spec = inputs.case_spec(case_id)
+    seeded row samples of every sequence checked against the oracle.  With the
+    V heads scaled (the workload as specified) the error is divided by
+    max(1, s_v); with V unscaled (q and k still scaled per head, which is what
+    stresses QK-Norm) the literal absolute bounds 2e-2 max / 2e-3 mean hold."""
+    spec = inputs.case_spec(case_id, v_scaled=v_scaled)
     U.say(f"prefill config {case_id} full size: {spec.workload} (generating inputs)")
     x = inputs.prefill_inputs(spec)
     U.say(f"prefill config {case_id} full size: launching ({spec.n_tok} tokens)")
@@ -257,6 +300,9 @@ def test_prefill_full_size_sampled(case_id):
         ref = U.oracle_rows(spec, s, rows, heads)
         got = U.down(out[cu[s] + rows])
         print(case_id, s, U.bf16_gate(got, ref, spec, label=f"config {case_id} seq {s}"))
+        if not v_scaled:
+            err = np.abs(got - ref)
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
 
 
 # ------------------------------------------------------------------ append (chunked prefill)
@@ -503,10 +549,12 @@ def test_decode_capacity_rejection_leaves_cache():
     assert torch.equal(kc, k0) and torch.equal(vc, v0)
 
 
-def test_decode_config2_full_size_sampled():
+@pytest.mark.parametrize("v_scaled", [True, False], ids=["v-scaled", "v-unscaled"])
+def test_decode_config2_full_size_sampled(v_scaled):
     """Qwen3-8B decode, 64 sequences with contexts U[1024, 32768], in the
-    benchmark's launch configuration; 4 sequences checked against the oracle."""
-    spec = inputs.case_spec(2)
+    benchmark's launch configuration; 4 sequences checked against the oracle
+    (unscaled V: the literal absolute bounds)."""
+    spec = inputs.case_spec(2, v_scaled=v_scaled)
     x = inputs.decode_new_token(spec)
     cap = (max(spec.lengths) + 1 + 63) // 64 * 64
     U.say(f"decode config 2: building cache ({sum(spec.lengths)} tokens, capacity {cap})")
@@ -522,4 +570,8 @@ def test_decode_config2_full_size_sampled():
     U.say(f"decode config 2: oracle for sequences {seqs}")
     raws = inputs.decode_cache_raw_all(spec, seqs)
     ref = U.oracle_decode(spec, x, raws, seqs)
-    print(U.bf16_gate(U.down(out[seqs]), ref, spec, label="config 2"))
+    got = U.down(out[seqs])
+    print(U.bf16_gate(got, ref, spec, label="config 2"))
+    if not v_scaled:
+        err = np.abs(got - ref)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
