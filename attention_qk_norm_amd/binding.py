@@ -60,6 +60,8 @@ def load(path=None):
     lib.qwattn_prefill.restype = i32
     lib.qwattn_decode.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, i32, vp, vp, sz, vp]
     lib.qwattn_decode.restype = i32
+    lib.qwattn_decode_noalloc.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, i32, vp, vp]
+    lib.qwattn_decode_noalloc.restype = i32
     lib.qwattn_append.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, pc, vp, ip, vp, ip, i32, vp, vp, sz, vp]
     lib.qwattn_append.restype = i32
     lib.qwattn_append_workspace_size.argtypes = [pp, i32, i32, i64, i32]
@@ -288,6 +290,28 @@ def decode(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, start
                              ctypes.c_void_p(start_pos.data_ptr()),
                              sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n_seq, _ptr(out),
                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def decode_noalloc(params, q, k, v, q_gamma, k_gamma, k_cache, v_cache, start_pos, start_pos_host=None, out=None):
+    """qwattn_decode without a workspace: the library's fixed device scratch
+    (QWATTN_DECODE_NOALLOC_SCRATCH_BYTES per device) instead."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_gamma, "q_gamma"), (k_gamma, "k_gamma"),
+                 (start_pos, "start_pos")):
+        _dev(t, n)
+    if start_pos_host is None:
+        start_pos_host = start_pos.cpu()
+    sp_h = torch.as_tensor(start_pos_host, dtype=torch.int32).contiguous()
+    if out is None:
+        out = _out_like(params, q)
+    _check_cache_pair(params, k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    _check(lib.qwattn_decode_noalloc(ctypes.byref(params), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(q_gamma),
+                                     _ptr(k_gamma), _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                                     ctypes.c_void_p(start_pos.data_ptr()),
+                                     sp_h.numpy().ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), sp_h.numel(),
+                                     _ptr(out), _stream()))
     return out
 
 

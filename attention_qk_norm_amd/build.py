@@ -19,7 +19,7 @@ LIB = os.path.join(LIBDIR, "libqwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qwattn_api.cpp", "k_normrope.hip", "k_prefill.hip", "k_prefill_wide.hip", "k_attn_f32.hip", "k_decode.hip",
-           "k_gemm.hip", "k_probe.hip"]
+           "k_gemm.hip", "k_probe.hip", "k_scratch.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code (the host pass of
 # hipcc warns that it does not know the feature; that is harmless).

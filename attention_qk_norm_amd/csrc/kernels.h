@@ -163,6 +163,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t st);
 
+// ---------------------------------------------------------------- fixed scratch
+// Device scratch for the entry points that allocate nothing: this many bytes
+// per device, at the address decode_scratch returns for the current device
+// (looked up once per device; shared by every such call on that device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // ---------------------------------------------------------------- measurement aids
 hipError_t launch_mfma_probe(int n_wg, int iters4, float* sink, hipStream_t st);
 hipError_t launch_read_probe(int n_wg, const void* src, int64_t n16, float* sink, hipStream_t st);

@@ -599,6 +599,141 @@ hipError_t launch_linear(const void* x, const void* w, int64_t m, int n, int k, 
   return qw::launch_gemm(g, qw::kGemmPlain, strm);
 }
 
+// ------------------------------------------------------------------ decode
+struct DecodeArgsIn {
+  const qwattn_params* params;
+  qwattn_dtype dtype;
+  const void *q, *k, *v, *q_gamma, *k_gamma;
+  void *k_cache, *v_cache;
+  const qwattn_cache_desc* cache;
+  const int32_t *start_pos, *start_pos_host;
+  int32_t n_seq;
+  void* out;
+};
+
+struct DecodeCall {
+  DecodeLayout dl;
+  int64_t total_chunks = 0;
+};
+
+// Every check of a decode call (nothing is enqueued); n_seq == 0 passes.
+qwattn_status decode_check(const DecodeArgsIn& in, DecodeCall& dc) {
+  const qwattn_params* params = in.params;
+  qwattn_status st;
+  if ((st = check_params(params, in.dtype))) return st;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  if (in.dtype == QWATTN_BF16 && g > 16) return fail(QWATTN_ERR_UNSUPPORTED, "decode group size %d > 16", g);
+  if (in.dtype == QWATTN_F32 && g > qw::kAttnF32Rows)
+    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d for fp32", g, qw::kAttnF32Rows);
+  if (in.n_seq < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_seq < 0");
+  if (in.n_seq == 0) return QWATTN_OK;
+  if ((st = check_ptr(in.q, "q")) || (st = check_ptr(in.k, "k")) || (st = check_ptr(in.v, "v")) ||
+      (st = check_ptr(in.q_gamma, "q_gamma")) || (st = check_ptr(in.k_gamma, "k_gamma")) ||
+      (st = check_ptr(in.out, "out")) || (st = check_ptr(in.start_pos, "start_pos", 4)))
+    return st;
+  if (!in.start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos_host is NULL");
+  if ((st = check_cache(in.cache, in.k_cache, in.v_cache, in.dtype, params->head_dim, in.n_seq, params->n_kv_heads)))
+    return st;
+  int64_t total = 0;
+  for (int i = 0; i < in.n_seq; ++i) {
+    const int sp = in.start_pos_host[i];
+    if (sp < 0) return fail(QWATTN_ERR_INVALID_ARG, "start_pos[%d] = %d < 0", i, sp);
+    if ((int64_t)sp + 1 > in.cache->capacity)
+      return fail(QWATTN_ERR_CAPACITY, "sequence %d: start_pos %d + 1 exceeds cache capacity %d", i, sp,
+                  in.cache->capacity);
+    total += sp;
+  }
+  dc.dl = decode_layout(params, in.dtype, in.n_seq, total);
+  dc.total_chunks = 0;
+  for (int i = 0; i < in.n_seq; ++i) dc.total_chunks += ((int64_t)in.start_pos_host[i] + dc.dl.chunk) / dc.dl.chunk;
+  if (dc.total_chunks * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many chunks");
+  return QWATTN_OK;
+}
+
+// The launches of a checked decode call, with its scratch at ws (dc.dl.total bytes).
+qwattn_status decode_launch(const DecodeArgsIn& in, const DecodeCall& dc, char* ws, hipStream_t strm) {
+  const qwattn_params* params = in.params;
+  const DecodeLayout& dl = dc.dl;
+  const int g = params->n_q_heads / params->n_kv_heads;
+  const int64_t D = params->head_dim;
+  const qwattn_cache_desc* cache = in.cache;
+  const void* gate = params->output_gate ? (const char*)in.q + D * elem_bytes(in.dtype) : nullptr;
+
+  // 1) prologue: q̂ -> scratch; k̂ (rotated at start_pos) and v -> cache slot start_pos
+  qw::NormRopeArgs nr{};
+  nr.x[0] = in.q; nr.x[1] = in.k; nr.x[2] = in.v;
+  nr.out[0] = ws + dl.off_qhat;
+  nr.out[1] = nullptr;
+  nr.gamma[0] = in.q_gamma; nr.gamma[1] = in.k_gamma;
+  nr.heads[0] = params->n_q_heads;
+  nr.heads[1] = params->n_kv_heads;
+  nr.heads[2] = params->n_kv_heads;
+  nr.k_cache = in.k_cache; nr.v_cache = in.v_cache;
+  nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
+  nr.pos = in.start_pos;
+  nr.n_seq = in.n_seq;
+  nr.mode = qw::kPosDecode;
+  nr.n_tok = in.n_seq;
+  set_norm(nr, params);
+  hipError_t e = qw::launch_normrope(in.dtype == QWATTN_BF16, nr, strm);
+  if (e != hipSuccess) return hip_fail(e, "decode prologue launch");
+
+  if (in.dtype == QWATTN_BF16) {
+    qw::DecodeArgs a{};
+    a.qhat = (const uint16_t*)(ws + dl.off_qhat);
+    a.gate = (const uint16_t*)gate;
+    a.q_row = q_row(params);
+    a.head_dim = params->head_dim;
+    a.k_cache = (const uint16_t*)in.k_cache;
+    a.v_cache = (const uint16_t*)in.v_cache;
+    a.cs_seq = cache->stride_seq; a.cs_head = cache->stride_head; a.cs_tok = cache->stride_tok;
+    a.start_pos = in.start_pos;
+    a.chunk_off = (const int32_t*)(ws + dl.off_chunk);
+    a.chunk_seq = (const int32_t*)(ws + dl.off_chunk_seq);
+    a.partial = (float*)(ws + dl.off_part);
+    a.out = (uint16_t*)in.out;
+    a.n_seq = in.n_seq;
+    a.Hq = params->n_q_heads;
+    a.Hkv = params->n_kv_heads;
+    a.g = g;
+    a.chunk = dl.chunk;
+    a.scale_log2e = scale_log2e(params);
+    if ((e = qw::launch_decode_plan(in.start_pos, in.n_seq, dl.chunk, (int)dl.max_chunks,
+                                    (int32_t*)(ws + dl.off_chunk), (int32_t*)(ws + dl.off_chunk_seq), strm)) !=
+        hipSuccess)
+      return hip_fail(e, "decode plan launch");
+    if ((e = timed_launch(strm, [&] { return qw::launch_decode_split(a, (int)dc.total_chunks, strm); })) !=
+        hipSuccess)
+      return hip_fail(e, "decode split launch");
+    if ((e = qw::launch_decode_combine(a, strm)) != hipSuccess) return hip_fail(e, "decode combine launch");
+  } else {
+    qw::PrefillArgs a{};
+    a.qhat = ws + dl.off_qhat;
+    a.gate = gate;
+    a.q_row = q_row(params);
+    a.head_dim = params->head_dim;
+    a.khat = in.k_cache;
+    a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
+    a.k_packed = 0;
+    a.v = in.v_cache;
+    a.vs_seq = cache->stride_seq; a.vs_head = cache->stride_head; a.vs_tok = cache->stride_tok;
+    a.v_packed = 0;
+    a.start_pos = in.start_pos;
+    a.out = in.out;
+    a.n_seq = in.n_seq;
+    a.Hq = params->n_q_heads;
+    a.Hkv = params->n_kv_heads;
+    a.g = g;
+    a.bm_tok = 1;
+    a.decode = 1;
+    a.scale_log2e = scale_log2e(params);
+    a.eps = params->eps;
+    if ((e = timed_launch(strm, [&] { return qw::launch_attn_f32(a, in.n_seq, strm); })) != hipSuccess)
+      return hip_fail(e, "decode attention launch");
+  }
+  return QWATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -642,114 +777,39 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype, con
                             const qwattn_cache_desc* cache, const int32_t* start_pos, const int32_t* start_pos_host,
                             int32_t n_seq, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
+  const DecodeArgsIn in{params, dtype, q, k, v, q_gamma, k_gamma, k_cache, v_cache, cache, start_pos, start_pos_host,
+                        n_seq, out};
+  DecodeCall dc;
   qwattn_status st;
-  if ((st = check_params(params, dtype))) return st;
-  const int g = params->n_q_heads / params->n_kv_heads;
-  if (dtype == QWATTN_BF16 && g > 16) return fail(QWATTN_ERR_UNSUPPORTED, "decode group size %d > 16", g);
-  if (dtype == QWATTN_F32 && g > qw::kAttnF32Rows)
-    return fail(QWATTN_ERR_UNSUPPORTED, "group size %d > %d for fp32", g, qw::kAttnF32Rows);
-  if (n_seq < 0) return fail(QWATTN_ERR_INVALID_ARG, "n_seq < 0");
+  if ((st = decode_check(in, dc))) return st;
   if (n_seq == 0) return QWATTN_OK;
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
-      (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(out, "out")) ||
-      (st = check_ptr(start_pos, "start_pos", 4)))
-    return st;
-  if (!start_pos_host) return fail(QWATTN_ERR_INVALID_ARG, "start_pos_host is NULL");
-  if ((st = check_cache(cache, k_cache, v_cache, dtype, params->head_dim, n_seq, params->n_kv_heads))) return st;
-  int64_t total = 0;
-  for (int i = 0; i < n_seq; ++i) {
-    const int sp = start_pos_host[i];
-    if (sp < 0) return fail(QWATTN_ERR_INVALID_ARG, "start_pos[%d] = %d < 0", i, sp);
-    if ((int64_t)sp + 1 > cache->capacity)
-      return fail(QWATTN_ERR_CAPACITY, "sequence %d: start_pos %d + 1 exceeds cache capacity %d", i, sp,
-                  cache->capacity);
-    total += sp;
-  }
-  const DecodeLayout dl = decode_layout(params, dtype, n_seq, total);
-  int64_t total_chunks = 0;
-  for (int i = 0; i < n_seq; ++i) total_chunks += ((int64_t)start_pos_host[i] + dl.chunk) / dl.chunk;
-  if (total_chunks * params->n_kv_heads > 0x7fffffffLL) return fail(QWATTN_ERR_UNSUPPORTED, "too many chunks");
   if (!workspace || !aligned(workspace, 256))
     return fail(QWATTN_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < dl.total)
-    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, dl.total);
+  if (workspace_bytes < dc.dl.total)
+    return fail(QWATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, dc.dl.total);
+  return decode_launch(in, dc, (char*)workspace, (hipStream_t)stream);
+}
 
-  hipStream_t strm = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int64_t D = params->head_dim;
-  const void* gate = params->output_gate ? (const char*)q + D * elem_bytes(dtype) : nullptr;
-
-  // 1) prologue: q̂ -> workspace; k̂ (rotated at start_pos) and v -> cache slot start_pos
-  qw::NormRopeArgs nr{};
-  nr.x[0] = q; nr.x[1] = k; nr.x[2] = v;
-  nr.out[0] = ws + dl.off_qhat;
-  nr.out[1] = nullptr;
-  nr.gamma[0] = q_gamma; nr.gamma[1] = k_gamma;
-  nr.heads[0] = params->n_q_heads;
-  nr.heads[1] = params->n_kv_heads;
-  nr.heads[2] = params->n_kv_heads;
-  nr.k_cache = k_cache; nr.v_cache = v_cache;
-  nr.cs_seq = cache->stride_seq; nr.cs_head = cache->stride_head; nr.cs_tok = cache->stride_tok;
-  nr.pos = start_pos;
-  nr.n_seq = n_seq;
-  nr.mode = qw::kPosDecode;
-  nr.n_tok = n_seq;
-  set_norm(nr, params);
-  hipError_t e = qw::launch_normrope(dtype == QWATTN_BF16, nr, strm);
-  if (e != hipSuccess) return hip_fail(e, "decode prologue launch");
-
-  if (dtype == QWATTN_BF16) {
-    qw::DecodeArgs a{};
-    a.qhat = (const uint16_t*)(ws + dl.off_qhat);
-    a.gate = (const uint16_t*)gate;
-    a.q_row = q_row(params);
-    a.head_dim = params->head_dim;
-    a.k_cache = (const uint16_t*)k_cache;
-    a.v_cache = (const uint16_t*)v_cache;
-    a.cs_seq = cache->stride_seq; a.cs_head = cache->stride_head; a.cs_tok = cache->stride_tok;
-    a.start_pos = start_pos;
-    a.chunk_off = (const int32_t*)(ws + dl.off_chunk);
-    a.chunk_seq = (const int32_t*)(ws + dl.off_chunk_seq);
-    a.partial = (float*)(ws + dl.off_part);
-    a.out = (uint16_t*)out;
-    a.n_seq = n_seq;
-    a.Hq = params->n_q_heads;
-    a.Hkv = params->n_kv_heads;
-    a.g = g;
-    a.chunk = dl.chunk;
-    a.scale_log2e = scale_log2e(params);
-    if ((e = qw::launch_decode_plan(start_pos, n_seq, dl.chunk, (int)dl.max_chunks, (int32_t*)(ws + dl.off_chunk),
-                                    (int32_t*)(ws + dl.off_chunk_seq), strm)) != hipSuccess)
-      return hip_fail(e, "decode plan launch");
-    if ((e = timed_launch(strm, [&] { return qw::launch_decode_split(a, (int)total_chunks, strm); })) != hipSuccess)
-      return hip_fail(e, "decode split launch");
-    if ((e = qw::launch_decode_combine(a, strm)) != hipSuccess) return hip_fail(e, "decode combine launch");
-  } else {
-    qw::PrefillArgs a{};
-    a.qhat = ws + dl.off_qhat;
-    a.gate = gate;
-    a.q_row = q_row(params);
-    a.head_dim = params->head_dim;
-    a.khat = k_cache;
-    a.ks_seq = cache->stride_seq; a.ks_head = cache->stride_head; a.ks_tok = cache->stride_tok;
-    a.k_packed = 0;
-    a.v = v_cache;
-    a.vs_seq = cache->stride_seq; a.vs_head = cache->stride_head; a.vs_tok = cache->stride_tok;
-    a.v_packed = 0;
-    a.start_pos = start_pos;
-    a.out = out;
-    a.n_seq = n_seq;
-    a.Hq = params->n_q_heads;
-    a.Hkv = params->n_kv_heads;
-    a.g = g;
-    a.bm_tok = 1;
-    a.decode = 1;
-    a.scale_log2e = scale_log2e(params);
-    a.eps = params->eps;
-    if ((e = timed_launch(strm, [&] { return qw::launch_attn_f32(a, n_seq, strm); })) != hipSuccess)
-      return hip_fail(e, "decode attention launch");
-  }
-  return QWATTN_OK;
+qwattn_status qwattn_decode_noalloc(const qwattn_params* params, qwattn_dtype dtype, const void* q, const void* k,
+                                    const void* v, const void* q_gamma, const void* k_gamma, void* k_cache,
+                                    void* v_cache, const qwattn_cache_desc* cache, const int32_t* start_pos,
+                                    const int32_t* start_pos_host, int32_t n_seq, void* out, void* stream) {
+  static_assert(qw::kNoAllocScratchBytes == QWATTN_DECODE_NOALLOC_SCRATCH_BYTES, "scratch size");
+  g_last_error.clear();
+  const DecodeArgsIn in{params, dtype, q, k, v, q_gamma, k_gamma, k_cache, v_cache, cache, start_pos, start_pos_host,
+                        n_seq, out};
+  DecodeCall dc;
+  qwattn_status st;
+  if ((st = decode_check(in, dc))) return st;
+  if (n_seq == 0) return QWATTN_OK;
+  if (dc.dl.total > qw::kNoAllocScratchBytes)
+    return fail(QWATTN_ERR_WORKSPACE,
+                "qwattn_decode_noalloc: these sizes need %zu bytes of scratch; the fixed scratch holds %zu "
+                "(call qwattn_decode with a workspace)",
+                dc.dl.total, (size_t)qw::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (const hipError_t e = qw::decode_scratch(&scratch)) return hip_fail(e, "fixed scratch lookup");
+  return decode_launch(in, dc, (char*)scratch, (hipStream_t)stream);
 }
 
 qwattn_status qwattn_mfma_probe(int32_t iters, float* sink, void* stream) {

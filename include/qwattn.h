@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define QWATTN_ABI_VERSION 5
+#define QWATTN_ABI_VERSION 6
 #define QWATTN_HEAD_DIM 128        /* Qwen3 layers                  */
 #define QWATTN_HEAD_DIM_GATED 256  /* gated Qwen3-Next / 3.5 layers */
 
@@ -178,6 +178,29 @@ qwattn_status qwattn_decode(const qwattn_params* params, qwattn_dtype dtype,
                             const int32_t* start_pos, const int32_t* start_pos_host,
                             int32_t n_seq, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* qwattn_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and kernels, without a workspace.  Its scratch is a
+ * fixed array of QWATTN_DECODE_NOALLOC_SCRATCH_BYTES in every device's global
+ * memory, part of the library's code object (held from its load until the
+ * process ends); the first call on a device looks its address up.  The call
+ * allocates and frees nothing.
+ *   Sizes whose qwattn_decode_workspace_size exceeds that maximum are rejected
+ *   with QWATTN_ERR_WORKSPACE and nothing enqueued (at 32 query / 8 KV heads,
+ *   head_dim 128, bf16: about 7.9 million cached keys in all for 64 sequences;
+ *   use qwattn_decode beyond).
+ *   Nothing in the scratch needs to start at zero.  All calls on one device
+ *   share the array: calls that overlap in time on one device (different
+ *   streams, or different threads) race and must be serialised by the caller.
+ *   A failed lookup of the array returns QWATTN_ERR_HIP. */
+#define QWATTN_DECODE_NOALLOC_SCRATCH_BYTES 67108864
+qwattn_status qwattn_decode_noalloc(const qwattn_params* params, qwattn_dtype dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const void* q_gamma, const void* k_gamma,
+                                    void* k_cache, void* v_cache, const qwattn_cache_desc* cache,
+                                    const int32_t* start_pos, const int32_t* start_pos_host,
+                                    int32_t n_seq, void* out, void* stream);
 
 /* Multi-token append (chunked prefill) against a KV cache: the new tokens of
  * each sequence attend to its cached keys and causally to each other, the mask

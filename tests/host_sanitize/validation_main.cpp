@@ -155,6 +155,13 @@ void decode_cases() {
           EXPECT(qwattn_decode(&p, dt, D, D, D, D, D, D, D, &c, (int32_t*)D, sp, n_seq, D2, ws.p, ws.n, nullptr) ==
                  QWATTN_OK);
           EXPECT(launched() >= 2);
+          // the same call on the fixed scratch, when its sizes fit there
+          int64_t tot = 0;
+          for (int i = 0; i < n_seq; ++i) tot += sp[i];
+          const bool fits = qwattn_decode_workspace_size(&p, dt, n_seq, tot) <= QWATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+          EXPECT(qwattn_decode_noalloc(&p, dt, D, D, D, D, D, D, D, &c, (int32_t*)D, sp, n_seq, D2, nullptr) ==
+                 (fits ? QWATTN_OK : QWATTN_ERR_WORKSPACE));
+          EXPECT(fits ? launched() >= 2 : launched() == 0);
         }
         sp[3] = 300001;  // start_pos + 1 > capacity
         EXPECT(qwattn_decode(&p, dt, D, D, D, D, D, D, D, &c, (int32_t*)D, sp, n_seq, D2, ws.p, ws.n, nullptr) ==
@@ -168,6 +175,20 @@ void decode_cases() {
         EXPECT(launched() == 0);
         delete[] sp;
       }
+}
+
+void noalloc_limit_cases() {
+  // 16 query / 1 KV head: the scratch of about 16.3 million keys fills the array
+  const qwattn_params p = params(16, 1);
+  for (int32_t each : {16000000, 16500000}) {
+    int32_t* sp = new int32_t[1]{each};
+    const qwattn_cache_desc c = cache(1, each + 1, 128);
+    const qwattn_status st =
+        qwattn_decode_noalloc(&p, QWATTN_BF16, D, D, D, D, D, D, D, &c, (int32_t*)D, sp, 1, D2, nullptr);
+    EXPECT(st == (each == 16000000 ? QWATTN_OK : QWATTN_ERR_WORKSPACE));
+    EXPECT(launched() == (each == 16000000 ? 4 : 0));
+    delete[] sp;
+  }
 }
 
 void layer_and_linear_cases() {
@@ -274,6 +295,7 @@ int main() {
   prefill_cases();
   append_cases();
   decode_cases();
+  noalloc_limit_cases();
   layer_and_linear_cases();
   if (failures) {
     std::fprintf(stderr, "%d of %d checks failed\n", failures, checks);

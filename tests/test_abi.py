@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qwattn_abi_version() == 5
+    assert lib.qwattn_abi_version() == 6
     for st in range(6):
         assert lib.qwattn_status_str(st)
 
@@ -269,3 +269,32 @@ def test_decode_workspace_size_is_monotone(lib):
                     sz = B.decode_workspace_size(p, dt, n_seq, t)
                     assert sz >= prev, (hkv, dt, d, n_seq, t, sz, prev)
                     prev = sz
+
+
+def test_decode_noalloc_validation_and_size_limit(lib):
+    """The no-allocation decode validates like qwattn_decode, and sizes whose
+    scratch exceeds the fixed array are rejected before anything is enqueued
+    (no GPU is touched: the check precedes the scratch lookup)."""
+    p = B.make_params(32, 8)
+    d = B.CacheDesc(8 * 100 * 128, 100 * 128, 128, 100)
+    f = lib.qwattn_decode_noalloc
+    assert f(ctypes.byref(p), 1, F, F, F, F, F, F, F, ctypes.byref(d), F, cu(3, 99, 100), 3, F, None) == B.ERR_CAPACITY
+    assert f(ctypes.byref(B.make_params(64, 2)), 1, F, F, F, F, F, F, F, ctypes.byref(d), F, cu(3), 1, F,
+             None) == B.ERR_UNSUPPORTED
+    assert f(ctypes.byref(p), 1, None, None, None, None, None, None, None, None, None, None, 0, None, None) == B.OK
+    limit = 67108864
+    # the largest total whose scratch fits, and one more chunk's worth
+    p16 = B.make_params(16, 1)
+    # (only over-limit sizes are called: a call that passed every check would
+    # launch kernels, and these pointers are fake)
+    for n_seq, total, ok in ((1, 16_000_000, True), (1, 16_500_000, False), (2, 8_300_000 * 2, False)):
+        need = B.decode_workspace_size(p16, B.BF16, n_seq, total)
+        assert (need <= limit) == ok, (n_seq, total, need)
+        if ok:
+            continue
+        each = total // n_seq
+        sp = (ctypes.c_int32 * n_seq)(*([each] * n_seq))
+        big = B.CacheDesc((each + 1) * 128, (each + 1) * 128, 128, each + 1)
+        r = f(ctypes.byref(p16), 1, F, F, F, F, F, F, F, ctypes.byref(big), F, sp, n_seq, F, None)
+        assert r == B.ERR_WORKSPACE
+        assert b"fixed scratch" in lib.qwattn_last_error()
