@@ -84,8 +84,8 @@ __device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* 
 // i + ROT/2 of a rotation pair sit in fragments kk and kk + ROT/32 of the same
 // lane; fragments from ROT/16 on pass unrotated.
 template <int ROT>
-__device__ __forceinline__ void q_prologue(const PrefillArgs& a, const u32x4 (&raw)[16], bool ok, int pos, int hg,
-                                           bf16x8 (&frag)[16]) {
+__device__ __forceinline__ void q_prologue(const PrefillArgs& a, const u32x4 (&raw)[16], const u32x4 (&graw)[16],
+                                           bool ok, int pos, int hg, bf16x8 (&frag)[16]) {
   constexpr int RH = ROT / 32;
   float x[16][8];
 #pragma unroll
@@ -102,9 +102,8 @@ __device__ __forceinline__ void q_prologue(const PrefillArgs& a, const u32x4 (&r
     for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
   ss = pair_sum(ss);  // lane l ^ 32 holds the other half of the row
   const float inv = rsqrtf(ss * (1.0f / kW) + a.eps);
-  const uint16_t* gq = (const uint16_t*)a.q_gamma + 8 * hg;
   auto scale = [&](int kk) __attribute__((always_inline)) {
-    const u32x4 gr = *reinterpret_cast<const u32x4*>(gq + 16 * kk);
+    const u32x4 gr = graw[kk];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[kk][2 * e] *= inv * (a.gamma_offset + bf16_lo(gr[e]));
@@ -212,14 +211,17 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(src + 16 * kk);
   }
+  u32x4 graw[16];  // the norm weights at the same dims, requested with the rows
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) graw[kk] = *reinterpret_cast<const u32x4*>((const uint16_t*)a.q_gamma + 8 * hg + 16 * kk);
   issue_tile(0, 0);
   bf16x8 qf[16];
   const int qp = valid ? qpos : 0;
   switch (a.rot) {
-    case 32: q_prologue<32>(a, qraw, valid, qp, hg, qf); break;
-    case 64: q_prologue<64>(a, qraw, valid, qp, hg, qf); break;
-    case 128: q_prologue<128>(a, qraw, valid, qp, hg, qf); break;
-    default: q_prologue<256>(a, qraw, valid, qp, hg, qf); break;
+    case 32: q_prologue<32>(a, qraw, graw, valid, qp, hg, qf); break;
+    case 64: q_prologue<64>(a, qraw, graw, valid, qp, hg, qf); break;
+    case 128: q_prologue<128>(a, qraw, graw, valid, qp, hg, qf); break;
+    default: q_prologue<256>(a, qraw, graw, valid, qp, hg, qf); break;
   }
   const bool use_static = a.static_flag[0] != 0;
   // Static-bound form: each tile's score accumulators start at -B (B the
@@ -440,6 +442,27 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
   // reciprocal (1 ulp) before the single rounding to bf16.
   constexpr int kORow = 4 * kW + 16;  // bytes per staged fp32 row (16 B pad)
   static_assert(128 * kORow <= kSmem, "the staged rows fit in the ring");
+  // Output chunks (16 B of 8 dims), ordered (token, head, chunk): thread tid
+  // takes chunks tid + 256 i.  Their gate values are requested first, all at
+  // once, so that one memory latency overlaps the staging below instead of
+  // one per few chunks in the store loop.
+  constexpr int kChunkIters = 128 * (kW / 8) / 256;
+  const int n_chunks = a.bm_tok * a.g * (kW / 8);
+  // row / g by one multiply: (row + 1/2) / g lies at least 1/(2g) >= 2^-9 from
+  // an integer and the float error is below 2^-15 for row < 256.
+  const float inv_g = 1.0f / (float)a.g;
+  u32x4 gate_raw[kChunkIters];
+  if (a.gate) {
+#pragma unroll
+    for (int i = 0; i < kChunkIters; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 5, part = c & 31;
+      const int tf = (int)(((float)row + 0.5f) * inv_g), hf = row - tf * a.g;
+      const bool ok = c < n_chunks && tok_base + tf < L;
+      const int64_t grow = (int64_t)(seq0 + (ok ? tok_base + tf : 0)) * a.Hq + u * a.g + (ok ? hf : 0);
+      gate_raw[i] = *reinterpret_cast<const u32x4*>((const uint16_t*)a.gate + grow * a.q_row + 8 * part);
+    }
+  }
   const float inv_l = 1.0f / pair_sum(l_run);
   __syncthreads();
   {
@@ -455,22 +478,19 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
       }
   }
   __syncthreads();
-  const int n_chunks = a.bm_tok * a.g * (kW / 8);  // 8-dim chunks, ordered (token, head, chunk)
-  // row / g by one multiply: (row + 1/2) / g lies at least 1/(2g) >= 2^-9 from
-  // an integer and the float error is below 2^-15 for row < 256.
-  const float inv_g = 1.0f / (float)a.g;
-#pragma unroll 4
-  for (int c = tid; c < n_chunks; c += 256) {
+#pragma unroll
+  for (int i = 0; i < kChunkIters; ++i) {
+    const int c = tid + 256 * i;
     const int row = c >> 5, part = c & 31;
     const int tf = (int)(((float)row + 0.5f) * inv_g), hf = row - tf * a.g;
-    if (tok_base + tf < L) {
+    if (c < n_chunks && tok_base + tf < L) {
       const lds_u8* src = lds + (hf * a.bm_tok + tf) * kORow + 32 * part;
       const f32x4 y0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src);
       const f32x4 y1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(src + 16);
       float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
       const int64_t grow = (int64_t)(seq0 + tok_base + tf) * a.Hq + u * a.g + hf;
       if (a.gate) {  // times sigmoid(gate) at the same dims
-        const u32x4 gr = *reinterpret_cast<const u32x4*>((const uint16_t*)a.gate + grow * a.q_row + 8 * part);
+        const u32x4 gr = gate_raw[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           y[2 * e] *= __builtin_amdgcn_rcpf(1.0f + __expf(-bf16_lo(gr[e])));

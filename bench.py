@@ -210,6 +210,22 @@ def run_decode(st):
              out=st["out"], workspace=st["ws"])
 
 
+def warm_up(run, seconds=0.3, max_calls=4000):
+    """Calls `run` for `seconds` of wall time (at least twice) before a timed
+    measurement: after the host-side input generation has left the GPU idle,
+    its clock takes a fraction of a second of load to come back up, and calls
+    timed earlier run up to 20% slow."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or (time.perf_counter() - t0 < seconds and n < max_calls):
+        run()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def _timed_lists(run, n_calls):
     """Per-call times (torch events around the call) and dominant-kernel times
     (the library's timing hook: HIP events on its stream), in ms."""
@@ -234,12 +250,11 @@ def _timed(run, n_calls):
     return float(np.mean(c)), float(np.mean(k))
 
 
-def measure_prefill_workload(case_id, dev, n_calls=10, warmup=2):
+def measure_prefill_workload(case_id, dev, n_calls=20):
     """One prefill workload on its own: warm-up calls, then n_calls timed."""
     import torch
     st = setup_prefill(case_id, dev)
-    for _ in range(warmup):
-        run_prefill(st)
+    warm_up(lambda: run_prefill(st))
     c, k = _timed_lists(lambda: run_prefill(st), n_calls)
     rec = prefill_record(st["spec"], c, k)
     del st
@@ -247,7 +262,7 @@ def measure_prefill_workload(case_id, dev, n_calls=10, warmup=2):
     return rec
 
 
-def measure_append(dev, n_calls=10, new_tokens=512):
+def measure_append(dev, n_calls=20, new_tokens=512):
     """Chunked prefill against the cache (qwattn_append), on the 4 x 4096
     workload: each sequence's first 4096 - new_tokens tokens are prefilled into
     the cache, then its last new_tokens tokens are appended (timed; every call
@@ -278,8 +293,7 @@ def measure_append(dev, n_calls=10, new_tokens=512):
     ws = torch.empty(B.append_workspace_size(p, B.BF16, spec.n_seq, int(cu_new[-1]), new_tokens),
                      dtype=torch.uint8, device=dev)
     run = lambda: B.append(p, q, k, v, qg, kg, kc, vc, sp, cn, sp_h, cu_new, out=out, workspace=ws)
-    for _ in range(2):
-        run()
+    warm_up(run)
     ev = HipEvents()
     kev = [(ev.create(), ev.create()) for _ in range(n_calls)]
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
@@ -302,7 +316,7 @@ def measure_append(dev, n_calls=10, new_tokens=512):
                          "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
 
 
-def measure_gated(dev, n_calls=10):
+def measure_gated(dev, n_calls=20):
     """The gated global layer of Qwen3-Next (head_dim 256, 16 query / 2 KV heads,
     rotary 64 of 256, zero-centred norm, sigmoid output gate): prefill of
     4 x 4096 tokens into a cache, and one decode step of 64 sequences with
@@ -327,8 +341,7 @@ def measure_gated(dev, n_calls=10):
     ws = torch.empty(B.prefill_workspace_size(p, B.BF16, spec.n_seq, spec.n_tok, max(spec.lengths), True),
                      dtype=torch.uint8, device=dev)
     run = lambda: B.prefill(p, q, k, v, qg, kg, cu, cu_h, out=out, k_cache=kc, v_cache=vc, workspace=ws)
-    for _ in range(2):
-        run()
+    warm_up(run)
     c_ms, k_ms = _timed(run, n_calls)
     flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads, head_dim=256)
     res["prefill"] = {
@@ -362,8 +375,7 @@ def measure_gated(dev, n_calls=10):
     out = torch.empty(spec.n_seq, spec.n_q_heads, 256, dtype=bf, device=dev)
     ws = torch.empty(B.decode_workspace_size(p, B.BF16, spec.n_seq, int(sp_h.sum())), dtype=torch.uint8, device=dev)
     run = lambda: B.decode(p, q, k, v, qg, kg, kc, vc, sp, sp_h, out=out, workspace=ws)
-    for _ in range(2):
-        run()
+    warm_up(run)
     c_ms, k_ms = _timed(run, n_calls)
     kv = accounting.decode_kv_read_bytes(spec.lengths, spec.n_kv_heads, head_dim=256)
     res["decode"] = {
@@ -376,7 +388,7 @@ def measure_gated(dev, n_calls=10):
     return res
 
 
-def measure_layer(dev, n_calls=10):
+def measure_layer(dev, n_calls=20):
     """The whole attention sublayer of Qwen3-8B (hidden 4096, 32 / 8 heads) on
     the 4 x 4096 prefill with the cache write: the fused q/k/v projection, the
     core and o_proj in one qwattn_attention_layer call; the o_proj GEMM is also
@@ -401,12 +413,11 @@ def measure_layer(dev, n_calls=10):
     ws = torch.empty(B.attention_layer_workspace_size(p, B.BF16, hidden, spec.n_seq, spec.n_tok, max(spec.lengths),
                                                       True), dtype=torch.uint8, device=dev)
     run = lambda: B.attention_layer(p, x, w_qkv, w_o, gq, gk, cu, cu_h, y=y, k_cache=kc, v_cache=vc, workspace=ws)
-    for _ in range(2):
-        run()
+    warm_up(run)
     c_ms, qkv_ms = _timed(run, n_calls)
     o_in = torch.empty(spec.n_tok, spec.n_q_heads * 128, dtype=bf, device=dev).normal_()
     run_o = lambda: B.linear(o_in, w_o, y=y)
-    run_o()
+    warm_up(run_o)
     _, o_ms = _timed(run_o, n_calls)
     d = 128
     qkv_flops = 2 * spec.n_tok * hidden * (spec.n_q_heads + 2 * spec.n_kv_heads) * d
