@@ -4,7 +4,7 @@ appending new tokens against a cache of already-normed, already-rotated keys);
 (``oracle.layer``) the sublayer around it: the bias-free q/k/v projections
 before the core and o_proj after it; and (``oracle.gated``) the gated
 global-attention layer of Qwen3-Next / Qwen3.5: zero-centred norm, partial
-RoPE, per-head sigmoid output gate.
+RoPE, per-head sigmoid output gate, and its sublayer with the projections.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -50,4 +50,8 @@ from .gated import (  # noqa: F401
     gated_attention_prefill,
     gated_attention_prefill_rows,
     gated_attention_append,
+    gated_qkv_projection,
+    gated_attention_layer_prefill,
+    gated_attention_layer_prefill_rows,
+    gated_attention_layer_append,
 )

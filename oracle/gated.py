@@ -30,6 +30,7 @@ Nothing is rounded anywhere in this module.
 import numpy as np
 
 from . import attention as _A
+from . import layer as _L
 
 _f64 = _A._f64
 
@@ -150,3 +151,54 @@ def gated_attention_append(q_new, gate_new, k_new, v_new, q_w, k_w, k_hat_cache,
     vals = np.concatenate([v_cache, v_new], axis=0)
     out = _A._attend(qh, keys, vals, pos, np.arange(start + n), n_q_heads, n_kv_heads, sc)
     return out * sigmoid(gate_new), kh_new
+
+
+def gated_qkv_projection(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim=256):
+    """The gated layer's projections: q_proj gives 2 * head_dim values per
+    query head, split inside each head into query and gate ([NW] Qwen3-Next:
+    q_proj's width doubled, half query, half gate; [OZ] §20.4); k_proj and
+    v_proj as in the Qwen3 layers.  w_q is ``[n_q_heads * 2 * head_dim,
+    hidden]``.  Returns (q, gate, k, v)."""
+    q, gate = split_query_gate(_L.linear(x, w_q), n_q_heads, head_dim)
+    return (q, gate, _L.split_heads(_L.linear(x, w_k), n_kv_heads, head_dim),
+            _L.split_heads(_L.linear(x, w_v), n_kv_heads, head_dim))
+
+
+def gated_attention_layer_prefill(x, w_q, w_k, w_v, w_o, q_w, k_w, cu_seqlens, n_q_heads, n_kv_heads,
+                                  head_dim=256, eps=1e-6, theta=1e7, rot_dim=64, scale=None):
+    """The gated global-attention sublayer over packed sequences: the
+    projections above, the gated core, then o_proj on the gated heads
+    concatenated in order (the attention output is multiplied by
+    sigmoid(gate) before o_proj: [NW]; [OZ] §20.4).  x ``[n_tok, hidden]`` ->
+    ``[n_tok, hidden]``; w_o is ``[hidden, n_q_heads * head_dim]``."""
+    q, gate, k, v = gated_qkv_projection(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    o = gated_attention_prefill(q, gate, k, v, q_w, k_w, cu_seqlens, n_q_heads, n_kv_heads, eps=eps, theta=theta,
+                                rot_dim=rot_dim, scale=scale)
+    return _L.linear(_L.merge_heads(o), w_o)
+
+
+def gated_attention_layer_prefill_rows(x_seq, w_q, w_k, w_v, w_o, q_w, k_w, rows, n_q_heads, n_kv_heads,
+                                       head_dim=256, eps=1e-6, theta=1e7, rot_dim=64, scale=None):
+    """Selected output rows of ONE sequence, each by the same definition as
+    :func:`gated_attention_layer_prefill`; ``x_seq`` holds the sequence's
+    hidden rows 0 .. max(rows).  Returns ``[len(rows), hidden]``."""
+    x_seq = _f64(x_seq)
+    rows = np.asarray(rows, dtype=np.int64)
+    nk = int(rows.max()) + 1
+    q, gate = split_query_gate(_L.linear(x_seq[rows], w_q), n_q_heads, head_dim)
+    k = _L.split_heads(_L.linear(x_seq[:nk], w_k), n_kv_heads, head_dim)
+    v = _L.split_heads(_L.linear(x_seq[:nk], w_v), n_kv_heads, head_dim)
+    o = gated_attention_prefill_rows(q, gate, k, v, q_w, k_w, rows, range(n_q_heads), n_q_heads, n_kv_heads,
+                                     eps=eps, theta=theta, rot_dim=rot_dim, scale=scale)
+    return _L.linear(_L.merge_heads(o), w_o)
+
+
+def gated_attention_layer_append(x_new, w_q, w_k, w_v, w_o, q_w, k_w, k_hat_cache, v_cache, start_pos,
+                                 n_q_heads, n_kv_heads, head_dim=256, eps=1e-6, theta=1e7, rot_dim=64, scale=None):
+    """New tokens of ONE sequence through the gated sublayer against its cache
+    of ``start_pos`` normed and rotated keys and values.  Returns ``(y [n,
+    hidden], k_hat_new, v_new)``."""
+    q, gate, k, v = gated_qkv_projection(x_new, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    o, kh = gated_attention_append(q, gate, k, v, q_w, k_w, k_hat_cache, v_cache, start_pos, n_q_heads, n_kv_heads,
+                                   eps=eps, theta=theta, rot_dim=rot_dim, scale=scale)
+    return _L.linear(_L.merge_heads(o), w_o), kh, v

@@ -114,3 +114,19 @@ def layer_prefill(x, w_q, w_k, w_v, w_o, q_gamma, k_gamma, lengths, n_q_heads, n
     o = prefill(q, k, v, q_gamma, k_gamma, lengths, n_q_heads, n_kv_heads, eps, theta)
     merged = [[o[t][h][e] for h in range(n_q_heads) for e in range(head_dim)] for t in range(len(o))]
     return linear(merged, w_o)
+
+
+def gated_layer_prefill(x, w_q, w_k, w_v, w_o, q_w, k_w, lengths, n_q_heads, n_kv_heads, head_dim, eps, theta,
+                        rot):
+    """The gated sublayer: q_proj gives 2 * head_dim values per query head, the
+    first head_dim of them the query and the next head_dim the gate; k_proj
+    and v_proj split into heads of head_dim; the gated layer above; heads
+    concatenated in order; o_proj."""
+    qp = linear(x, w_q)
+    q = [[[r[2 * h * head_dim + e] for e in range(head_dim)] for h in range(n_q_heads)] for r in qp]
+    gate = [[[r[2 * h * head_dim + head_dim + e] for e in range(head_dim)] for h in range(n_q_heads)] for r in qp]
+    k = [[[r[h * head_dim + e] for e in range(head_dim)] for h in range(n_kv_heads)] for r in linear(x, w_k)]
+    v = [[[r[h * head_dim + e] for e in range(head_dim)] for h in range(n_kv_heads)] for r in linear(x, w_v)]
+    o = gated_prefill(q, gate, k, v, q_w, k_w, lengths, n_q_heads, n_kv_heads, eps, theta, rot)
+    merged = [[o[t][h][e] for h in range(n_q_heads) for e in range(head_dim)] for t in range(len(o))]
+    return linear(merged, w_o)

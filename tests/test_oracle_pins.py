@@ -236,3 +236,37 @@ def test_layer_planted_mistake_is_caught(name, monkeypatch):
         except (AssertionError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------------------------ the gated sublayer
+
+@pytest.mark.parametrize("pin", pins_layer.GATED_LAYER_PINS, ids=lambda f: f.__name__)
+def test_gated_layer_pin(pin):
+    pin()
+
+
+def _split_query_gate_swapped(q_proj_out, n_heads, head_dim):
+    y = np.asarray(q_proj_out, dtype=np.float64).reshape(-1, n_heads, 2 * head_dim)
+    return y[..., head_dim:], y[..., :head_dim]
+
+
+GATED_LAYER_MUTATIONS = {
+    "gate_split_across_heads": (G, "split_query_gate", _split_halves),
+    "query_gate_swapped": (G, "split_query_gate", _split_query_gate_swapped),
+    "linear_without_transpose": (Y, "linear", _linear_untransposed),
+    "split_heads_dim_major": (Y, "split_heads", _split_heads_dim_major),
+    "merge_heads_dim_major": (Y, "merge_heads", _merge_heads_dim_major),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GATED_LAYER_MUTATIONS))
+def test_gated_layer_planted_mistake_is_caught(name, monkeypatch):
+    mod, attr, fn = GATED_LAYER_MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    failed = []
+    for pin in pins_layer.GATED_LAYER_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
