@@ -3,7 +3,7 @@
 // Qwen3Attention excerpt: q_proj, k_proj, v_proj, o_proj; "7.2 Qwen3 全规模实现"
 // §7.2.1 listing).
 //
-// Two epilogues:
+// Three epilogues:
 //  * plain: y rounded to bf16 (o_proj, or any projection);
 //  * qkv: the fused q/k/v projection.  Its output columns are head blocks of
 //    128: Hq query heads, then Hkv key heads, then Hkv value heads (the three
@@ -12,7 +12,12 @@
 //    the token's position straight from the fp32 accumulators and written to
 //    the KV cache (or a packed buffer); value blocks go to the cache as they
 //    are.  So K and V reach HBM once, already in their cached form
-//    ("Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE).
+//    ("Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE);
+//  * gated qkv: the same for the gated global layers of Qwen3-Next / Qwen3.5
+//    (head_dim 256; "14. Qwen 家族" Qwen3-Next section; "第 20 章" §20.4):
+//    q_proj gives 2 x 256 values per query head, the query then the gate,
+//    written raw; key heads get the zero-centred norm (scale 1 + w) and the
+//    partial rotation of their leading dims; value heads go as they are.
 //
 // Tiling: a workgroup (8 waves, two per SIMD) computes a 256-token x
 // 256-column tile as C^T = W X^T with v_mfma_f32_32x32x16_bf16 (A = W
@@ -42,9 +47,10 @@ constexpr int kTile = 32 * kBlk;           // one 256 x 64 operand tile
 constexpr int kStageBytes = 2 * kTile;     // x tile, then W tile
 constexpr int kSmem = 2 * kStageBytes;     // two stages
 constexpr int kThreads = 512;              // 8 waves: two per SIMD
-// qkv: after the ring, the key norm scale (128 floats) and the RoPE
-// frequencies (64 doubles), read per lane in the epilogue.
-constexpr int kGammaOff = kSmem, kFreqOff = kSmem + 512, kSmemQkv = kSmem + 1024;
+// qkv: after the ring, the key norm scale (up to 256 floats) and the RoPE
+// frequencies (64 doubles), read per lane in the epilogue; gated qkv: then the
+// halves of the keys' sums of squares ([4 token quarters][2][32 tokens][2 halves]).
+constexpr int kGammaOff = kSmem, kFreqOff = kSmem + 1024, kSsOff = kSmem + 1536, kSmemQkv = kSmem + 1536 + 2048;
 static_assert(kSmemQkv <= 160 * 1024, "LDS per workgroup");
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
@@ -137,6 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   if constexpr (EPI == kGemmQkv) {  // published by the first barrier below
     if (tid < 128) gk_lds[tid] = bf16_to_f32(a.k_gamma[tid]);
     else if (tid < 192) w_lds[tid - 128] = a.rope.w[tid - 128];
+  } else if constexpr (EPI >= kGemmQkvGated) {
+    if (tid < 256) gk_lds[tid] = a.gamma_offset + bf16_to_f32(a.k_gamma[tid]);
+    else if (tid < 320) w_lds[tid - 256] = a.rope.w[tid - 256];
   }
   // K step 0 into LDS stage 0; K step 1 into the staging registers.
 #pragma unroll
@@ -195,6 +204,122 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   // ---- epilogue.  acc[jc][it][j]: token row0 + 64 wt + 32 it + n, column
   // col0 + 128 wc + 32 jc + 8 (j / 4) + 4 hg + j % 4.
   const int ccol = col0 + 128 * wc;  // the wave's first column (a head block in the qkv form)
+  // The gated q/k/v epilogue (head_dim 256).  Column regions -- tiles never
+  // straddle them, every width being a multiple of 256 -- are: Hq query rows of
+  // q_width values, written raw to q_out [M][Hq][q_width]; Hkv key heads, normed
+  // and partially rotated at each token's position; Hkv value heads.  A head of
+  // 256 spans the tile: wave (wt, wc) holds dims 128 wc .. 128 wc + 127 of its 64
+  // tokens, so a key's sum of squares adds the two waves' halves through LDS (the
+  // branch is uniform over the workgroup, so its barrier is too), and the
+  // rotated dims (at most 128) all lie in the waves with wc = 0.  acc[jc][it][j]:
+  // token row0 + 64 wt + 32 it + n, column 32 jc + 8 (j / 4) + 4 hg + j % 4 of the
+  // wave's 128.
+  if constexpr (EPI >= kGemmQkvGated) {
+    // one instantiation per rotary width: 32, 64 or 128 leading dims turn
+    constexpr int ROT = EPI == kGemmQkvGated ? 32 : EPI == kGemmQkvGated + 1 ? 64 : 128;
+    auto store128 = [&](uint16_t* dst, const float (&x)[4][16]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg)
+          *reinterpret_cast<u32x2*>(dst + 32 * jc + 8 * jg) =
+              u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
+    };
+    const int qcols = a.Hq * a.q_width;
+    if (col0 < qcols) {  // query (and gate) values, raw
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int64_t tok = row0 + 64 * wt + 32 * it + n;
+        if (tok >= a.M) continue;
+        float x[4][16];
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) x[jc][j] = acc[jc][it][j];
+        store128(a.q_out + tok * qcols + col0 + 128 * wc + 4 * hg, x);
+      }
+      return;
+    }
+    constexpr int D = kMaxD;
+    const bool is_k = col0 < qcols + a.Hkv * D;
+    const int kv = (col0 - qcols) / D - (is_k ? 0 : a.Hkv);
+    float inv[2] = {0.f, 0.f};
+    if (is_k) {
+      float* ss_lds = (float*)(smem + kSsOff);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        float ss = 0.f;
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) ss += acc[jc][it][j] * acc[jc][it][j];
+        ss = pair_sum(ss);  // lane n ^ 32 holds the other 64 of the wave's 128 dims
+        if (hg == 0) ss_lds[((wt * 2 + it) * 32 + n) * 2 + wc] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const float* p = ss_lds + ((wt * 2 + it) * 32 + n) * 2;
+        inv[it] = rsqrtf((p[0] + p[1]) * (1.0f / D) + a.eps);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int64_t tok = row0 + 64 * wt + 32 * it + n;
+      const bool valid = tok < a.M;
+      float x[4][16];
+#pragma unroll
+      for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[jc][j] = acc[jc][it][j];
+      int s = 0, pos = 0;
+      if (valid) token_position(a, tok, s, pos);
+      if (is_k) {
+        // norm scale 1 + w (the table holds gamma_offset + gamma); RMS is
+        // rotation-invariant, so one inv serves both orders
+        auto scale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+          for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[jc][j] *= inv[it] * gk_lds[128 * wc + 32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)];
+        };
+        // dims c and c + rot/2 (c < rot/2) turn by pos * w_c, the angle reduced
+        // in fp64 and evaluated by the hardware sine/cosine, which take turns
+        auto turn = [&](int jc1, int j1, int jc2, int j2) __attribute__((always_inline)) {
+          const int c = 32 * jc1 + 8 * (j1 >> 2) + 4 * hg + (j1 & 3);
+          const double t = (double)pos * (w_lds[c] * 0.15915494309189535);
+          const float r = (float)(t - rint(t));
+          const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
+          const float y1 = x[jc1][j1], y2 = x[jc2][j2];
+          x[jc1][j1] = y1 * cs - y2 * sn;
+          x[jc2][j2] = y2 * cs + y1 * sn;
+        };
+        if (a.order == 0) scale();
+        if (wc == 0) {
+          if constexpr (ROT == 128) {
+#pragma unroll
+            for (int jc = 0; jc < 2; ++jc)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) turn(jc, j, jc + 2, j);
+          } else if constexpr (ROT == 64) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) turn(0, j, 1, j);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) turn(0, j, 0, j + 8);
+          }
+        }
+        if (a.order != 0) scale();
+      }
+      if (!valid) continue;
+      uint16_t* cache = is_k ? a.k_cache : a.v_cache;
+      uint16_t* dst = cache ? cache + s * a.cs_seq + kv * a.cs_head + (int64_t)pos * a.cs_tok
+                            : (is_k ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * D;
+      store128(dst + 128 * wc + 4 * hg, x);
+    }
+
+    return;
+  }
   if (ccol >= a.N) return;
   if constexpr (EPI == kGemmPlain) {
 #pragma unroll
@@ -300,6 +425,11 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (epilogue == kGemmQkvGated) {
+    if (a.rot == 32) return launch_t<kGemmQkvGated>(a, st);
+    if (a.rot == 64) return launch_t<kGemmQkvGated + 1>(a, st);
+    return launch_t<kGemmQkvGated + 2>(a, st);
+  }
   return epilogue == kGemmQkv ? launch_t<kGemmQkv>(a, st) : launch_t<kGemmPlain>(a, st);
 }
 

@@ -135,8 +135,10 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 // y = x W^T, bf16 operands, fp32 accumulation.  x [M][K] (row stride ldx), W
 // [N][K] (row stride ldw); K a multiple of 64, N a multiple of 128.
 enum GemmEpilogue : int {
-  kGemmPlain = 0,  // y [M][N] (row stride ldy), rounded to bf16
-  kGemmQkv = 1,    // columns = Hq query, Hkv key, Hkv value head blocks of 128
+  kGemmPlain = 0,     // y [M][N] (row stride ldy), rounded to bf16
+  kGemmQkv = 1,       // columns = Hq query, Hkv key, Hkv value head blocks of 128
+  kGemmQkvGated = 2,  // columns = Hq query rows of q_width (query, then gate), Hkv key and Hkv
+                      // value heads of 256 (the gated layers)
 };
 struct GemmArgs {
   const uint16_t* x;
@@ -147,9 +149,13 @@ struct GemmArgs {
   uint16_t* y;              // plain
   int64_t ldy;
   int Hq, Hkv;              // qkv: head blocks
-  uint16_t* q_out;          // qkv: raw queries [M][Hq][128]
-  uint16_t* k_out;          // qkv: normed+rotated keys [M][Hkv][128] when k_cache is NULL
-  uint16_t* v_out;          // qkv: values [M][Hkv][128] when v_cache is NULL
+  int q_width;              // gated qkv: values per query head in the q_proj output (256, or 512
+                            // with the output gate: the query, then the gate)
+  int rot;                  // gated qkv: rotated leading dims of a key head (32, 64 or 128)
+  float gamma_offset;       // gated qkv: key norm scale = gamma_offset + gamma
+  uint16_t* q_out;          // qkv: raw queries [M][Hq][128] (gated: [M][Hq][q_width])
+  uint16_t* k_out;          // qkv: normed+rotated keys [M][Hkv][d] when k_cache is NULL
+  uint16_t* v_out;          // qkv: values [M][Hkv][d] when v_cache is NULL
   uint16_t* k_cache;        // qkv: cache rows (seq, head, pos) as in NormRopeArgs
   uint16_t* v_cache;
   int64_t cs_seq, cs_head, cs_tok;

@@ -541,7 +541,9 @@ qwattn_status prefill_or_append(const qwattn_params* params, qwattn_dtype dtype,
 }
 
 // Workspace of the sublayer: the prefill plan (and K̂ without a cache), then
-// raw q and the attention output (bf16, [n_tok][Hq][128]), and V without a cache.
+// raw q ([n_tok][Hq][q_row]: with the output gate each head's query, then its
+// gate), the attention output ([n_tok][Hq][head_dim]), and V without a cache;
+// all bf16.
 struct LayerPlan {
   PrefillPlan pl;
   size_t off_q = 0, off_o = 0, off_v = 0, total = 0;
@@ -552,11 +554,10 @@ LayerPlan layer_layout(const qwattn_params* p, int n_seq, int64_t n_tok, int max
   LayerPlan lp;
   lp.pl = prefill_layout(p, QWATTN_BF16, n_seq, n_tok, max_tiles, n_items, with_cache);
   size_t off = lp.pl.total;
-  const size_t qbytes = (size_t)n_tok * p->n_q_heads * p->head_dim * 2;
   lp.off_q = off;
-  off = align256(off + qbytes);
+  off = align256(off + (size_t)n_tok * p->n_q_heads * q_row(p) * 2);
   lp.off_o = off;
-  off = align256(off + qbytes);
+  off = align256(off + (size_t)n_tok * p->n_q_heads * p->head_dim * 2);
   lp.off_v = off;
   if (!with_cache) off = align256(off + (size_t)n_tok * p->n_kv_heads * p->head_dim * 2);
   lp.total = off;
@@ -578,12 +579,13 @@ qwattn_status check_layer_params(const qwattn_params* params, qwattn_dtype dtype
   qwattn_status st;
   if ((st = check_params(params, dtype))) return st;
   if (dtype != QWATTN_BF16) return fail(QWATTN_ERR_UNSUPPORTED, "the sublayer runs in bf16");
-  if (params->head_dim != QWATTN_HEAD_DIM)
-    return fail(QWATTN_ERR_UNSUPPORTED, "the sublayer runs at head_dim 128 (the Qwen3 layers)");
+  if (params->head_dim == QWATTN_HEAD_DIM_GATED && rot_dim(params) > 128)
+    return fail(QWATTN_ERR_UNSUPPORTED, "the head_dim-256 sublayer rotates at most 128 leading dims (rotary_dim=%d)",
+                rot_dim(params));
   if (hidden <= 0 || hidden % 128)
     return fail(hidden <= 0 ? QWATTN_ERR_INVALID_ARG : QWATTN_ERR_UNSUPPORTED,
                 "hidden=%d must be a positive multiple of 128", hidden);
-  // the q/k/v projection reads rows of hidden values, o_proj rows of Hq * 128
+  // the q/k/v projection reads rows of hidden values, o_proj rows of Hq * head_dim
   return check_gemm_shape(0, 0, std::max<int64_t>(hidden, (int64_t)params->n_q_heads * params->head_dim));
 }
 
@@ -890,7 +892,8 @@ qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype d
       (st = check_ptr(q_gamma, "q_gamma")) || (st = check_ptr(k_gamma, "k_gamma")) || (st = check_ptr(y, "y")))
     return st;
   if (sp.n_tok == 0) return QWATTN_OK;
-  if ((st = check_gemm_shape(sp.n_tok, (int64_t)(params->n_q_heads + 2 * params->n_kv_heads) * params->head_dim,
+  if ((st = check_gemm_shape(sp.n_tok,
+                             (int64_t)params->n_q_heads * q_row(params) + 2 * params->n_kv_heads * params->head_dim,
                              hidden)))
     return st;
   const LayerPlan lp = layer_layout(params, n_seq, sp.n_tok, sp.max_tiles, sp.n_items, sp.any_cache);
@@ -900,13 +903,16 @@ qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype d
   char* ws = (char*)workspace;
   const int D = params->head_dim, Hq = params->n_q_heads, Hkv = params->n_kv_heads;
 
-  // 1) x W_qkv^T: raw q -> workspace; K̂ (normed, rotated at each token's
-  // position) and V -> the cache, or packed workspace buffers
+  // 1) x W_qkv^T: raw q (and gate) -> workspace; K̂ (normed, rotated at each
+  // token's position) and V -> the cache, or packed workspace buffers
   qw::GemmArgs g{};
   g.x = (const uint16_t*)x;
   g.w = (const uint16_t*)w_qkv;
   g.M = sp.n_tok;
-  g.N = (Hq + 2 * Hkv) * D;
+  g.N = Hq * q_row(params) + 2 * Hkv * D;
+  g.q_width = q_row(params);
+  g.rot = rot_dim(params);
+  g.gamma_offset = params->norm_offset;
   g.K = hidden;
   g.ldx = hidden; g.ldw = hidden;
   g.Hq = Hq; g.Hkv = Hkv;
@@ -925,10 +931,11 @@ qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype d
   g.eps = params->eps;
   g.order = params->order;
   g.rope = rope_freq(params);
-  hipError_t e = timed_launch(strm, [&] { return qw::launch_gemm(g, qw::kGemmQkv, strm); });
+  const int epi = D == QWATTN_HEAD_DIM ? qw::kGemmQkv : qw::kGemmQkvGated;
+  hipError_t e = timed_launch(strm, [&] { return qw::launch_gemm(g, epi, strm); });
   if (e != hipSuccess) return hip_fail(e, "qkv projection launch");
 
-  // 2) plan + attention -> O [n_tok][Hq][128] in the workspace
+  // 2) plan + attention -> O [n_tok][Hq][head_dim] in the workspace
   const KvSource kv = sp.any_cache ? cache_source(cache, k_cache, v_cache)
                                    : packed_source(ws + lp.pl.off_khat, ws + lp.off_v, params);
   if ((st = launch_attention(params, dtype, ws + lp.off_q, q_gamma, k_gamma, kv, cu_seqlens, start_pos, n_seq, sp,

@@ -168,9 +168,12 @@ def gated_case_spec(case_id):
 
 
 # The attention sublayer of Qwen3-8B (hidden 4096, 32 / 8 heads) at the
-# 4 x 4096 prefill shape.
+# 4 x 4096 prefill shape, and the gated global-attention sublayer of
+# Qwen3-Next-80B-A3B (hidden 2048, 16 / 2 heads of 256, 25% rotary, theta 1e7)
+# at the same token shape.
 LAYER_CASE = 7
-LAYER_HIDDEN = {LAYER_CASE: 4096}
+GATED_LAYER_CASE = 8
+LAYER_HIDDEN = {LAYER_CASE: 4096, GATED_LAYER_CASE: 2048}
 
 
 def layer_case_spec():
@@ -178,6 +181,11 @@ def layer_case_spec():
     spec.case_id = LAYER_CASE
     spec.workload = "qwen3-8b-attention-sublayer-bf16 B4 T4096 hidden4096 Hq32 Hkv8"
     return spec
+
+
+def gated_layer_case_spec():
+    return gated_spec(GATED_LAYER_CASE, "bf16", 16, 2, [4096] * 4, rot=64,
+                      workload="qwen3-next-gated-sublayer-bf16 B4 T4096 hidden2048 Hq16 Hkv2 d256 rot64")
 
 
 def _weight(spec, stream, rows, cols):
@@ -193,10 +201,13 @@ def _weight(spec, stream, rows, cols):
 
 
 def layer_weights(spec, hidden):
-    """(w_qkv [(Hq + 2 Hkv) d, hidden], w_o [hidden, Hq d]): the stacked q/k/v
-    projection weights and the o_proj weight, each stored [out][in]."""
+    """(w_qkv [Hq q_w + 2 Hkv d, hidden], w_o [hidden, Hq d]): the stacked q/k/v
+    projection weights and the o_proj weight, each stored [out][in]; q_w = d,
+    or 2 d for a gated layer (per query head its query rows, then its gate
+    rows)."""
     d = spec.head_dim
-    return (_weight(spec, S_WQKV, (spec.n_q_heads + 2 * spec.n_kv_heads) * d, hidden),
+    q_w = 2 * d if spec.gated else d
+    return (_weight(spec, S_WQKV, spec.n_q_heads * q_w + 2 * spec.n_kv_heads * d, hidden),
             _weight(spec, S_WO, hidden, spec.n_q_heads * d))
 
 

@@ -14,7 +14,8 @@ the decode KV-read GB/s sits under ``decode``.  The other prefill workloads
 after the steps, each with its own roofline, under ``prefill_workloads``.
 The line also carries chunked-prefill (``append``), the gated head_dim-256
 layer of Qwen3-Next (``gated``: prefill and decode) and the whole attention
-sublayer with its projections (``layer``) figures, and the CPU oracle timed on
+sublayer with its projections (``layer`` for Qwen3-8B, ``gated_layer`` for
+the Qwen3-Next global-attention sublayer) figures, and the CPU oracle timed on
 bounded samples (``cpu_baseline`` for the long prefill, ``decode.cpu_baseline``).
 
     python bench.py [--steps K] [--warmup W] [--prefill-case {1,3,4}] [--extra-prefill 1,4|none]
@@ -388,26 +389,35 @@ def measure_gated(dev, n_calls=20):
     return res
 
 
-def measure_layer(dev, n_calls=20):
-    """The whole attention sublayer of Qwen3-8B (hidden 4096, 32 / 8 heads) on
-    the 4 x 4096 prefill with the cache write: the fused q/k/v projection, the
-    core and o_proj in one qwattn_attention_layer call; the o_proj GEMM is also
-    timed on its own through qwattn_linear."""
+def measure_layer(dev, n_calls=20, gated=False):
+    """A whole attention sublayer on the 4 x 4096 prefill with the cache write:
+    the fused q/k/v projection, the core and o_proj in one
+    qwattn_attention_layer call; the o_proj GEMM is also timed on its own
+    through qwattn_linear.  Qwen3-8B (hidden 4096, 32 / 8 heads of 128), or
+    with ``gated`` the global-attention sublayer of Qwen3-Next-80B-A3B (hidden
+    2048, 16 / 2 heads of 256, q_proj giving each head's query and gate,
+    rotary 64, sigmoid output gate)."""
     import torch
     from attention_qk_norm_amd import accounting, binding as B, inputs
     bf = torch.bfloat16
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
-    spec = inputs.layer_case_spec()
+    spec = inputs.gated_layer_case_spec() if gated else inputs.layer_case_spec()
     hidden = inputs.LAYER_HIDDEN[spec.case_id]
+    d = spec.head_dim
+    q_w = 2 * d if gated else d
     log(f"sublayer workload: {spec.workload}")
     w_qkv, w_o = inputs.layer_weights(spec, hidden)
     x = up(inputs.layer_x(spec, hidden))
     w_qkv, w_o = up(w_qkv), up(w_o)
     gq, gk = (up(g) for g in inputs.gammas(spec))
-    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    if gated:
+        p = B.make_gated_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta,
+                                rotary_dim=spec.rot)
+    else:
+        p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
     cu_h = spec.cu_seqlens()
     cu = torch.from_numpy(cu_h).to(dev)
-    kc = torch.empty(spec.n_seq, spec.n_kv_heads, max(spec.lengths), 128, dtype=bf, device=dev)
+    kc = torch.empty(spec.n_seq, spec.n_kv_heads, max(spec.lengths), d, dtype=bf, device=dev)
     vc = torch.empty_like(kc)
     y = torch.empty(spec.n_tok, hidden, dtype=bf, device=dev)
     ws = torch.empty(B.attention_layer_workspace_size(p, B.BF16, hidden, spec.n_seq, spec.n_tok, max(spec.lengths),
@@ -415,23 +425,25 @@ def measure_layer(dev, n_calls=20):
     run = lambda: B.attention_layer(p, x, w_qkv, w_o, gq, gk, cu, cu_h, y=y, k_cache=kc, v_cache=vc, workspace=ws)
     warm_up(run)
     c_ms, qkv_ms = _timed(run, n_calls)
-    o_in = torch.empty(spec.n_tok, spec.n_q_heads * 128, dtype=bf, device=dev).normal_()
+    o_in = torch.empty(spec.n_tok, spec.n_q_heads * d, dtype=bf, device=dev).normal_()
     run_o = lambda: B.linear(o_in, w_o, y=y)
     warm_up(run_o)
     _, o_ms = _timed(run_o, n_calls)
-    d = 128
-    qkv_flops = 2 * spec.n_tok * hidden * (spec.n_q_heads + 2 * spec.n_kv_heads) * d
+    qkv_flops = 2 * spec.n_tok * hidden * (spec.n_q_heads * q_w + 2 * spec.n_kv_heads * d)
     o_flops = 2 * spec.n_tok * spec.n_q_heads * d * hidden
-    attn_flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    attn_flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads, head_dim=d)
     total = qkv_flops + attn_flops + o_flops
     gemm = lambda f, ms: {"achieved": round(f / (ms * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(f / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                           "kernel_ms": round(ms, 4), "algorithmic_flops": f}
-    return {"metric": "attention sublayer TFLOP/s (q/k/v projection + core + o_proj)", "unit": "TFLOP/s",
+    kname = "k_gemm_qkv_gated" if gated else "k_gemm_qkv"
+    what = "query|gate, k, v" if gated else "q/k/v"
+    return {"metric": f"attention sublayer TFLOP/s ({what} projection + core + o_proj)", "unit": "TFLOP/s",
             "workload": spec.workload, "value": round(total / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
             "algorithmic_flops": total,
-            "roofline": dict(kernel="k_gemm<qkv> (fused q/k/v projection)", bound="mfma", **gemm(qkv_flops, qkv_ms),
-                             traffic=recorded_traffic("k_gemm_qkv", "k_gemm.hip", spec.workload)),
+            "roofline": dict(kernel=f"k_gemm<{'qkv_gated' if gated else 'qkv'}> (fused {what} projection)",
+                             bound="mfma", **gemm(qkv_flops, qkv_ms),
+                             traffic=recorded_traffic(kname, "k_gemm.hip", spec.workload)),
             "o_proj": dict(kernel="k_gemm<plain> via qwattn_linear", bound="mfma", **gemm(o_flops, o_ms),
                            traffic=recorded_traffic("k_gemm_plain", "k_gemm.hip", spec.workload))}
 
@@ -544,7 +556,7 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the chunked-prefill (append) measurement")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-layer (head_dim 256) measurements")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-sublayer (projections) measurement")
-    ap.add_argument("--only", choices=["append", "gated", "layer"],
+    ap.add_argument("--only", choices=["append", "gated", "layer", "gated_layer"],
                     help="profiling aid: run only this measurement and print its record (no step, not a bench line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device-to-device copy kernel (counter calibration)")
@@ -561,7 +573,8 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     if args.only:
-        rec = {"append": measure_append, "gated": measure_gated, "layer": measure_layer}[args.only](dev)
+        rec = {"append": measure_append, "gated": measure_gated, "layer": measure_layer,
+               "gated_layer": lambda d: measure_layer(d, gated=True)}[args.only](dev)
         if args.copy_calibration:
             rec["copy_calibration_bytes"] = copy_calibration(dev)
         print(json.dumps({args.only: rec}), flush=True)
@@ -663,6 +676,10 @@ def main():
         torch.cuda.empty_cache()
         log("sublayer measurement")
         rec["layer"] = measure_layer(dev)
+        if not args.no_gated:
+            torch.cuda.empty_cache()
+            log("gated sublayer measurement")
+            rec["gated_layer"] = measure_layer(dev, gated=True)
     if args.copy_calibration:
         rec["copy_calibration_bytes"] = copy_calibration(dev)
     if not args.no_cpu_baseline:

@@ -250,15 +250,20 @@ qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, in
  * or an append against the cache: q/k/v projections, QK-Norm, RoPE, causal GQA
  * attention, o_proj ["Qwen3" notes: qkv_proj -> split -> RMSNorm(Q, K) -> RoPE
  * -> attention -> o_proj; "7.2 Qwen3 全规模实现" §7.2.1 listing: heads
- * concatenated in order before out_proj].
- *   hidden: model width (a multiple of 128, <= 8388608, as is n_q_heads * 128:
+ * concatenated in order before out_proj].  With params.head_dim 256 it is the
+ * gated global-attention sublayer of Qwen3-Next / Qwen3.5 ["14. Qwen 家族",
+ * Qwen3-Next section: q_proj's width doubled, half query and half gate;
+ * "第 20 章 Qwen3 与 Qwen3.5" §20.4: the split is inside each head].
+ *   hidden: model width (a multiple of 128, <= 8388608, as is n_q_heads * head_dim:
  *     the projections' inner dimensions); x [n_tok][hidden] (device): the
  *     layer input rows, packed as for qwattn_prefill.
- *   w_qkv [(n_q_heads + 2 n_kv_heads) * 128][hidden] (device): the q_proj, k_proj
- *     and v_proj weights (each stored [out][in]) stacked in that order; head h of
- *     a projection owns its output features h*128 .. h*128+127.
- *   w_o [hidden][n_q_heads * 128] (device): the o_proj weight.
- *   q_gamma, k_gamma [128] (device).
+ *   w_qkv [n_q_heads * q_w + 2 n_kv_heads * head_dim][hidden] (device): the
+ *     q_proj, k_proj and v_proj weights (each stored [out][in]) stacked in that
+ *     order; q_w = head_dim, or 2 * head_dim with params.output_gate, where
+ *     query head h owns q_proj outputs h*q_w .. h*q_w + q_w - 1: its query,
+ *     then its gate.  Key and value head h own outputs h*head_dim ..
+ *   w_o [hidden][n_q_heads * head_dim] (device): the o_proj weight.
+ *   q_gamma, k_gamma [head_dim] (device).
  *   cu_seqlens / cu_seqlens_host, n_seq: as for qwattn_prefill.
  *   start_pos, start_pos_host: NULL for a prefill (positions 0 ..), or both set
  *     for an append (as for qwattn_append; the cache is then required).
@@ -268,9 +273,10 @@ qwattn_status qwattn_linear(qwattn_dtype dtype, const void* x, const void* w, in
  *     slots of each token.
  *   workspace (device, >= qwattn_attention_layer_workspace_size, 256-byte
  *     aligned).
- * Only QWATTN_BF16 and head_dim 128 (QWATTN_ERR_UNSUPPORTED else); fp32
- * accumulation in every product; q, k, v, the attention output and y are each
- * rounded to bf16 once.  n_seq == 0 or n_tok == 0 is a no-op. */
+ * Only QWATTN_BF16 (QWATTN_ERR_UNSUPPORTED else); at head_dim 256 a
+ * rotary_dim of at most 128.  fp32 accumulation in every product; q (and the
+ * gate), k, v, the attention output and y are each rounded to bf16 once.
+ * n_seq == 0 or n_tok == 0 is a no-op. */
 qwattn_status qwattn_attention_layer(const qwattn_params* params, qwattn_dtype dtype, int32_t hidden,
                                      const void* x, const void* w_qkv, const void* w_o,
                                      const void* q_gamma, const void* k_gamma,

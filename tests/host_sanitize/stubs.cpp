@@ -121,9 +121,11 @@ hipError_t launch_gemm(const GemmArgs& a, int epilogue, hipStream_t) {
   if (epilogue == kGemmPlain) {
     stub::write(a.y, (size_t)a.M * a.ldy * 2);
   } else {
-    stub::write(a.q_out, (size_t)a.M * a.Hq * 128 * 2);
-    if (!a.k_cache) stub::write(a.k_out, (size_t)a.M * a.Hkv * 128 * 2);
-    if (!a.v_cache) stub::write(a.v_out, (size_t)a.M * a.Hkv * 128 * 2);
+    const size_t d = epilogue == kGemmQkvGated ? 256 : 128;
+    const size_t qw = epilogue == kGemmQkvGated ? (size_t)a.q_width : d;
+    stub::write(a.q_out, (size_t)a.M * a.Hq * qw * 2);
+    if (!a.k_cache) stub::write(a.k_out, (size_t)a.M * a.Hkv * d * 2);
+    if (!a.v_cache) stub::write(a.v_out, (size_t)a.M * a.Hkv * d * 2);
   }
   return hipSuccess;
 }

@@ -217,6 +217,25 @@ void layer_and_linear_cases() {
     }
     delete[] cu;
   }
+  // the gated sublayer (head_dim 256, query and gate per head), with and without the cache
+  for (int with_cache : {0, 1}) {
+    const qwattn_params pg = params(16, 2, 256);
+    const int n_seq = 3;
+    int32_t* cu = new int32_t[n_seq + 1]{0, 100, 100, 613};
+    stub::n_tok = 613;
+    const size_t need = qwattn_attention_layer_workspace_size(&pg, QWATTN_BF16, 2048, n_seq, 613, 513, with_cache);
+    EXPECT(need > 0);
+    HostWs ws(need);
+    const qwattn_cache_desc c = cache(2, 600, 256);
+    EXPECT(qwattn_attention_layer(&pg, QWATTN_BF16, 2048, D, D, D, D, D, (int32_t*)D, cu, n_seq, nullptr, nullptr,
+                                  D2, with_cache ? D : nullptr, with_cache ? D : nullptr, with_cache ? &c : nullptr,
+                                  ws.p, ws.n, nullptr) == QWATTN_OK);
+    EXPECT(launched() == 4);
+    delete[] cu;
+  }
+  qwattn_params pr = params(16, 2, 256);
+  pr.rotary_dim = 256;  // the fused gated projection rotates at most 128 dims
+  EXPECT(qwattn_attention_layer_workspace_size(&pr, QWATTN_BF16, 2048, 1, 5, 5, 0) == 0);
   EXPECT(qwattn_attention_layer(&p, QWATTN_F32, 4096, D, D, D, D, D, (int32_t*)D, nullptr, 0, nullptr, nullptr, D2,
                                 nullptr, nullptr, nullptr, nullptr, 0, nullptr) == QWATTN_ERR_UNSUPPORTED);
   EXPECT(qwattn_linear(QWATTN_BF16, D, D, 1000, 384, 4096, D2, nullptr) == QWATTN_OK);
