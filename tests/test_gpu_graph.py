@@ -107,18 +107,25 @@ def test_prefill_and_decode_replay_in_a_graph():
     assert bool(torch.isfinite(g_out.float()).all()) and bool(torch.isfinite(g_dout.float()).all())
 
 
-def test_attention_layer_replay_in_a_graph():
+@pytest.mark.parametrize("gated", [False, True], ids=["qwen3", "gated"])
+def test_attention_layer_replay_in_a_graph(gated):
     """The sublayer (q/k/v projection GEMM with the norm/RoPE/cache epilogue,
-    attention, o_proj GEMM) captured once and replayed on two input sets."""
-    hidden, lengths = 1024, [300, 129]
-    spec = inputs.custom_spec(154, "bf16", 16, 8, lengths)
+    attention, o_proj GEMM) captured once and replayed on two input sets: the
+    Qwen3 form (head_dim 128), and the gated form (head_dim 256: query|gate
+    rows, zero-centred key norm and partial rotation in the epilogue, whose
+    key heads add their sums of squares across waves through LDS)."""
+    hidden, lengths = (512, [300, 129]) if gated else (1024, [300, 129])
+    hq, hkv = (8, 2) if gated else (16, 8)
+    make = (lambda cid: inputs.gated_spec(cid, "bf16", hq, hkv, lengths, rot=64)) if gated else \
+        (lambda cid: inputs.custom_spec(cid, "bf16", hq, hkv, lengths))
+    spec = make(156 if gated else 154)
+    d = spec.head_dim
     w_qkv, w_o = inputs.layer_weights(spec, hidden)
     gq, gk = inputs.gammas(spec)
     bf = torch.bfloat16
-    xs = [U.up(inputs.layer_x(spec, hidden), bf), U.up(inputs.layer_x(inputs.custom_spec(155, "bf16", 16, 8, lengths),
-                                                                     hidden), bf)]
+    xs = [U.up(inputs.layer_x(spec, hidden), bf), U.up(inputs.layer_x(make(157 if gated else 155), hidden), bf)]
     w_qkv, w_o, gq, gk = U.up(w_qkv, bf), U.up(w_o, bf), U.up(gq, bf), U.up(gk, bf)
-    p = U.params(spec)
+    p = B.make_gated_params(hq, hkv, eps=spec.eps, rope_theta=spec.theta, rotary_dim=spec.rot) if gated else U.params(spec)
     cu_h = spec.cu_seqlens()
     cu = torch.from_numpy(cu_h).to(U.DEV)
     cap = max(lengths) + 5
@@ -126,7 +133,7 @@ def test_attention_layer_replay_in_a_graph():
                      dtype=torch.uint8, device=U.DEV)
     g_x = xs[0].clone()
     g_y = torch.empty(spec.n_tok, hidden, dtype=bf, device=U.DEV)
-    g_kc = torch.full((spec.n_seq, 8, cap, 128), 7.0, dtype=bf, device=U.DEV)
+    g_kc = torch.full((spec.n_seq, hkv, cap, d), 7.0, dtype=bf, device=U.DEV)
     g_vc = torch.full_like(g_kc, 7.0)
 
     def call(x, y, kc, vc):
