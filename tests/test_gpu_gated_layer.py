@@ -208,3 +208,48 @@ def test_gated_layer_full_size_sampled():
     err = np.abs(got - ref)
     print(f"gated sublayer full size: max {err.max():.3e} mean {err.mean():.3e}")
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_gated_layer_rope_then_norm():
+    """order = 1 at head_dim 256: the projection's key epilogue and the core's
+    query prologue rotate first and norm after (scale 1 + w applied after the
+    rotation).  Reference composed from the oracle's pinned pieces: the gated
+    projections, rope_partial, rms_norm_zero_centred, causal_softmax per head
+    with its KV group, sigmoid(gate), o_proj; the cached K̂ checked as well."""
+    hq, hkv, lengths, hidden, rot = 8, 2, [70, 129], 256, 64
+    spec, x, w_qkv, w_o, gq, gk = _inputs(305, hq, hkv, lengths, hidden, rot)
+    U.say("gated sublayer, RoPE then norm")
+    p = _params(spec)
+    p.order = 1
+    cu = spec.cu_seqlens()
+    kc = torch.zeros(spec.n_seq, hkv, max(lengths), D, dtype=BF, device=U.DEV)
+    vc = torch.zeros_like(kc)
+    y = B.attention_layer(p, U.up(x, BF), U.up(w_qkv, BF), U.up(w_o, BF), U.up(gq, BF), U.up(gk, BF),
+                          torch.from_numpy(cu).to(U.DEV), cu, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    qw = hq * 2 * D
+    q, gate, k, v = oracle.gated_qkv_projection(x, w_qkv[:qw], w_qkv[qw:qw + hkv * D], w_qkv[qw + hkv * D:], hq, hkv)
+    o = np.zeros(q.shape)
+    for s in range(spec.n_seq):
+        a, b = cu[s], cu[s + 1]
+        pos = np.arange(b - a)
+        qh = oracle.rms_norm_zero_centred(oracle.rope_partial(q[a:b], pos, spec.theta, rot), gq, spec.eps)
+        kh = oracle.rms_norm_zero_centred(oracle.rope_partial(k[a:b], pos, spec.theta, rot), gk, spec.eps)
+        for t in range(hq):
+            u = oracle.kv_head_for_q_head(t, hq, hkv)
+            pr = oracle.causal_softmax(qh[:, t] @ kh[:, u].T / np.sqrt(D), pos, pos)
+            o[a:b, t] = (pr @ v[a:b, u]) * oracle.sigmoid(gate[a:b, t])
+        # the projection's fp32 error carried through the rotation (norm-preserving)
+        # and the norm to first order, with the scale 1 + w, plus one bf16 rounding
+        wk = w_qkv[qw:qw + hkv * D].astype(np.float64)
+        kb = (hidden * 2.0 ** -23 * (np.abs(x[a:b]).astype(np.float64) @ np.abs(wk).T)).reshape(b - a, hkv, D)
+        kr = k[a:b]
+        rms = np.sqrt(np.mean(kr ** 2, axis=-1, keepdims=True) + spec.eps)
+        kbound = 2.0 * np.abs(1.0 + gk).max() * (kb.max(axis=-1, keepdims=True) / rms) * \
+            (1.0 + np.abs(kr).max(axis=-1, keepdims=True) / rms) + 2.0 ** -8 * np.abs(kh) + 1e-6
+        got_k = U.down(kc[s, :, :b - a].permute(1, 0, 2))
+        assert np.all(np.abs(got_k - kh) <= kbound), np.abs(got_k - kh).max()
+    ref = oracle.linear(oracle.merge_heads(o), w_o)
+    err = np.abs(U.down(y) - ref)
+    print(f"gated layer rope->norm: max {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
