@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 vector / MFMA (published)
 HEADLINE_PREFILL = 3             # the long prefill: 1 x 32768 tokens, 64 / 8 heads
 EXTRA_PREFILL = "1,4"            # the other prefill workloads, timed beside the steps
 
@@ -448,6 +449,34 @@ def measure_layer(dev, n_calls=20, gated=False):
                            traffic=recorded_traffic("k_gemm_plain", "k_gemm.hip", spec.workload))}
 
 
+def measure_fp32_parity(dev, n_calls=50):
+    """The fp32 parity workload (Qwen3-0.6B heads: 1 x 128 tokens, 16 / 8 heads,
+    fp32 in and out, fp32 arithmetic throughout): its time, and its share of
+    the fp32 peak as information only (67.6 MFLOP is a few microseconds of
+    work, so the launches dominate)."""
+    import torch
+    from attention_qk_norm_amd import accounting, binding as B, inputs
+    spec = inputs.case_spec(0)
+    x = inputs.prefill_inputs(spec)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, k, v, qg, kg = (up(x[n]) for n in ("q", "k", "v", "q_gamma", "k_gamma"))
+    cu_h = x["cu_seqlens"]
+    cu = torch.from_numpy(cu_h).to(dev)
+    p = B.make_params(spec.n_q_heads, spec.n_kv_heads, eps=spec.eps, rope_theta=spec.theta)
+    out = torch.empty_like(q)
+    ws = torch.empty(B.prefill_workspace_size(p, B.F32, spec.n_seq, spec.n_tok, max(spec.lengths), False),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: B.prefill(p, q, k, v, qg, kg, cu, cu_h, out=out, workspace=ws)
+    warm_up(run, seconds=0.1)
+    c_ms, k_ms = _timed(run, n_calls)
+    flops = accounting.prefill_flops(spec.lengths, spec.n_q_heads)
+    return {"metric": "fp32 prefill TFLOP/s (parity workload; information only)", "unit": "TFLOP/s",
+            "workload": spec.workload, "dtype": "f32", "value": round(flops / (c_ms * 1e-3) / 1e12, 4),
+            "call_ms": round(c_ms, 4), "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops,
+            "kernel_frac_fp32_peak": round(flops / (k_ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 5),
+            "fp32_peak_tflops": FP32_PEAK_TFLOPS}
+
+
 def copy_calibration(dev):
     """One 1 GiB device-to-device copy, whose counter readings scale the
     FETCH_SIZE / WRITE_SIZE figures of a counter run."""
@@ -680,6 +709,8 @@ def main():
             torch.cuda.empty_cache()
             log("gated sublayer measurement")
             rec["gated_layer"] = measure_layer(dev, gated=True)
+    log("fp32 parity workload")
+    rec["fp32_parity"] = measure_fp32_parity(dev)
     if args.copy_calibration:
         rec["copy_calibration_bytes"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
