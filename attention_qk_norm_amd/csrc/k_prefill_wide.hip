@@ -28,7 +28,7 @@
 //
 // K/V tiles of 64 keys (32 KB each) go HBM -> LDS directly
 // (global_load_lds_dwordx4) into a two-stage ring: tile t+1 lands while tile t
-// is used.
+// is used, its copies issued one per two score MFMAs of tile t.
 //
 // Softmax: as in the head_dim-128 kernel, the query rows are pre-multiplied by
 // c = scale * log2(e); when the launch-wide bound c * 256 * max|scale_q| *
@@ -187,19 +187,38 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   // Wave w fills blocks 8w .. 8w+7 of K and of V.  Keys past n_kv (last tile
   // only) repeat the last key: they are masked, and stay finite.
-  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
-    const uint32_t kdst = lds0 + stage * kStageBytes;
-    const uint32_t vdst = kdst + kKTile;
-    const char* kt = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
-    const char* vt = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
+  // TileCopy: one tile's copies for this lane, addresses formed in advance so
+  // the static tile can issue them one at a time between its MFMAs.
+  struct TileCopy {
+    uint32_t kdst, vdst;
+    const char *ksrc, *vsrc;
+    uint32_t ko[kBlocksPerWave], vo[kBlocksPerWave];
+  };
+  auto tile_copy = [&](int t, int stage) __attribute__((always_inline)) {
+    TileCopy c;
+    c.kdst = lds0 + stage * kStageBytes + wu * kBlocksPerWave * kKBlk;
+    c.vdst = lds0 + stage * kStageBytes + kKTile + wu * kBlocksPerWave * kVBlk;
+    c.ksrc = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
+    c.vsrc = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
     const int last = n_kv - 1 - t * kTileKeys;  // last valid row of the tile
 #pragma unroll
     for (int m = 0; m < kBlocksPerWave; ++m) {
-      const int blk = wu * kBlocksPerWave + m;
-      const int row = min(blk + 32 * (lane >> 5), last);
-      load_lds16_async(kdst + blk * kKBlk, kt, (uint32_t)(row * kstride) + (lane & 31) * 16);
-      load_lds16_async(vdst + blk * kVBlk, vt, (uint32_t)(row * vstride) + (lane & 31) * 16);
+      const int row = min(wu * kBlocksPerWave + m + 32 * (lane >> 5), last);
+      c.ko[m] = (uint32_t)(row * kstride) + (lane & 31) * 16;
+      c.vo[m] = (uint32_t)(row * vstride) + (lane & 31) * 16;
     }
+    return c;
+  };
+  // copy i (0 .. 15) of a tile: K block 8w + i/2 (i even), V block 8w + i/2 (i odd)
+  auto issue_copy = [&](const TileCopy& c, int i) __attribute__((always_inline)) {
+    const int m = i >> 1;
+    if (i & 1) load_lds16_async(c.vdst + m * kVBlk, c.vsrc, c.vo[m]);
+    else load_lds16_async(c.kdst + m * kKBlk, c.ksrc, c.ko[m]);
+  };
+  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    const TileCopy c = tile_copy(t, stage);
+#pragma unroll
+    for (int i = 0; i < 2 * kBlocksPerWave; ++i) issue_copy(c, i);
   };
   const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
 
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
   // middle phases, by half a weight pair; sched_barrier keeps the compiler
   // from regrouping them.
   constexpr int kLead = 6;
-  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag) __attribute__((always_inline)) {
+  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag, const TileCopy& next) __attribute__((always_inline)) {
     constexpr bool kDiag = decltype(diag_tag)::value;
     f32x16 sacc[2];
     bf16x8 pf[4];
@@ -378,6 +397,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
     for (int kk = 0; kk < 16; ++kk) {  // S(keys 0-31)
       smfma(0, kk);
       fread(kk + kLead);
+      if (kk & 1) issue_copy(next, kk >> 1);
       fence();
     }
 #pragma unroll
@@ -385,6 +405,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
       smfma(1, kk);
       if (kk & 1) weights(0, kk >> 1);
       fread(16 + kk + kLead);
+      if (kk & 1) issue_copy(next, 8 + (kk >> 1));
       fence();
     }
 #pragma unroll
@@ -410,17 +431,25 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
       // of tile t-1, which receives tile t+1.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
       const int key0 = t * kTileKeys;
-      if (key0 > wave_max) continue;  // every key of the tile is in this wave's future
       const lds_u8* ks = lds + (t & 1) * kStageBytes;
       constexpr bool kStatic = decltype(static_tag)::value;
-      if constexpr (kStatic) {
+      if (kStatic && key0 <= wave_max) {
+        // The static tile issues tile t+1's 16 copies one per two score MFMAs
+        // over its first half rather than in a burst here: a burst fills the
+        // copy queue and stalls the in-order issue of the first MFMAs.  Past
+        // the last tile it copies the last tile again into the free stage (in
+        // bounds, never read), so the tile has no branch.
+        const TileCopy next = tile_copy(min(t + 1, n_tiles - 1), (t + 1) & 1);
         if (key0 + kTileKeys - 1 > wave_min)
-          static_tile(ks, ks + kKTile, key0, std::true_type{});
+          static_tile(ks, ks + kKTile, key0, std::true_type{}, next);
         else
-          static_tile(ks, ks + kKTile, key0, std::false_type{});
-      } else {
+          static_tile(ks, ks + kKTile, key0, std::false_type{}, next);
+        continue;
+      }
+      if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
+      if (key0 > wave_max) continue;  // every key of the tile is in this wave's future
+      if constexpr (!kStatic) {
         if (key0 + kTileKeys - 1 > wave_min)
           tile(ks, ks + kKTile, key0, static_tag, std::true_type{});
         else
@@ -432,6 +461,8 @@ __global__ __launch_bounds__(256, 1) void k_prefill_wide(const PrefillItem* __re
     run(std::true_type{});
   else
     run(std::false_type{});
+  // the repeat copies issued during the last tile land before the ring is reused
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of
   // row n.  The normalised rows are staged in LDS as fp32 (the ring is free
