@@ -24,7 +24,7 @@
 //
 // K/V tiles of 64 keys go HBM -> LDS directly (global_load_lds_dwordx4, no
 // staging registers) into a three-stage ring: tiles t+1 and t+2 land while tile
-// t is used.
+// t is used, tile t+2's copies issued during tile t's first MFMAs.
 //
 // Softmax: QK-Norm bounds every logit.  The query rows are pre-multiplied by
 // c = scale * log2(e) before their bf16 rounding, so the MFMA scores are in
@@ -159,24 +159,42 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
   }
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
-    const uint32_t kdst = lds0 + stage * kStageBytes;
-    const uint32_t vdst = kdst + kKTile;
-    const char* kt = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
-    const char* vt = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
+  // TileCopy: one tile's copies for this lane (K blocks 4w .. 4w+3, then V),
+  // addresses formed in advance so the static tile can issue them one at a
+  // time between its MFMAs.
+  struct TileCopy {
+    uint32_t kdst, vdst;
+    const char *ksrc, *vsrc;
+    uint32_t off[kLoadsPerTile];
+  };
+  auto tile_copy = [&](int t, int stage) __attribute__((always_inline)) {
+    TileCopy c;
+    c.kdst = lds0 + stage * kStageBytes + wu * 4 * kKBlk;
+    c.vdst = lds0 + stage * kStageBytes + kKTile + wu * 4 * kVBlk;
+    c.ksrc = (const char*)kbase + (int64_t)t * kTileKeys * kstride;
+    c.vsrc = (const char*)vbase + (int64_t)t * kTileKeys * vstride;
     const bool tail = (t + 1) * kTileKeys > n_kv;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int blk = wu * 4 + m;
-      uint32_t ko = koff[m], vo = voff[m];
+      c.off[m] = koff[m];
+      c.off[4 + m] = voff[m];
       if (tail) {
         const int r = min(w * 4 + m + 16 * (lane >> 4), n_kv - 1 - t * kTileKeys);
-        ko = (uint32_t)(r * kstride) + (lane & 15) * 16;
-        vo = (uint32_t)(r * vstride) + (lane & 15) * 16;
+        c.off[m] = (uint32_t)(r * kstride) + (lane & 15) * 16;
+        c.off[4 + m] = (uint32_t)(r * vstride) + (lane & 15) * 16;
       }
-      load_lds16_async(kdst + blk * kKBlk, kt, ko);
-      load_lds16_async(vdst + blk * kVBlk, vt, vo);
     }
+    return c;
+  };
+  // copy i (0 .. 7): K block 4w + i (i < 4), then V block 4w + i - 4
+  auto issue_copy = [&](const TileCopy& c, int i) __attribute__((always_inline)) {
+    if (i < 4) load_lds16_async(c.kdst + i * kKBlk, c.ksrc, c.off[i]);
+    else load_lds16_async(c.vdst + (i - 4) * kVBlk, c.vsrc, c.off[i]);
+  };
+  auto issue_tile = [&](int t, int stage) __attribute__((always_inline)) {
+    const TileCopy c = tile_copy(t, stage);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) issue_copy(c, i);
   };
   const int n_tiles = (n_kv + kTileKeys - 1) / kTileKeys;
 
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
   // is followed by a quarter of one weight group (two keys) for the VALU to
   // run under it, and every step issues the LDS fragment read that is needed
   // three steps later.  sched_barrier keeps the compiler from regrouping them.
-  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag) __attribute__((always_inline)) {
+  auto static_tile = [&](const lds_u8* ks, const lds_u8* vs, int key0, auto diag_tag, const TileCopy& next) __attribute__((always_inline)) {
     constexpr bool kDiag = decltype(diag_tag)::value;
     f32x16 sacc[2][2];  // [key block kb][query block qb]
     bf16x8 pf[2][4];    // [qb][16-key slice kk]
@@ -482,6 +500,7 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
       smfma(0, kk, 0);
       smfma(0, kk, 1);
       kread(kk + 3);
+      issue_copy(next, kk);  // tile t+2's copies, one per two MFMAs
       fence();
     }
     // S(keys 32-63) + weights of keys 0-31; then the first V fragments
@@ -534,24 +553,32 @@ __global__ __launch_bounds__(256, 1) void k_prefill_bf16(const PrefillItem* __re
       else
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      if (t + 2 < n_tiles) issue_tile(t + 2, stage == 0 ? 2 : stage - 1);
+      const int next = stage == 0 ? 2 : stage - 1;  // the stage tile t+2 goes to
       const int key0 = t * kTileKeys;
-      if (key0 > wave_max) continue;        // every key of the tile is in this wave's future
       const lds_u8* ks = lds + stage * kStageBytes;
-      if constexpr (kStatic) {
+      if (kStatic && key0 <= wave_max) {
+        // The static tile issues tile t+2's copies one per two MFMAs of its
+        // first phase rather than in a burst here.  Past the last tile it
+        // copies the last tile again into the free stage (in bounds, never
+        // read), so the tile has no branch.
+        const TileCopy nc = tile_copy(min(t + 2, n_tiles - 1), next);
         if (key0 + kTileKeys - 1 > wave_min)
-          static_tile(ks, ks + kKTile, key0, std::true_type{});
+          static_tile(ks, ks + kKTile, key0, std::true_type{}, nc);
         else
-          static_tile(ks, ks + kKTile, key0, std::false_type{});
-      } else {
-        tile(ks, ks + kKTile, key0);
+          static_tile(ks, ks + kKTile, key0, std::false_type{}, nc);
+        continue;
       }
+      if (t + 2 < n_tiles) issue_tile(t + 2, next);
+      if (key0 > wave_max) continue;        // every key of the tile is in this wave's future
+      if constexpr (!kStatic) tile(ks, ks + kKTile, key0);
     }
   };
   if (use_static)
     run(std::true_type{});
   else
     run(std::false_type{});
+  // the repeat copies issued during the last tiles land before the ring is reused
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // ---- epilogue: O^T block db, register j = dim 32db + 8(j/4) + 4hg + j%4 of
   // row (qb, n).  The normalised rows are staged in LDS (the ring is free once
