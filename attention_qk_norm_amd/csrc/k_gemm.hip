@@ -19,21 +19,33 @@
 //    written raw; key heads get the zero-centred norm (scale 1 + w) and the
 //    partial rotation of their leading dims; value heads go as they are.
 //
-// Tiling: a workgroup (8 waves, two per SIMD) computes a 256-token x
-// 256-column tile as C^T = W X^T with v_mfma_f32_32x32x16_bf16 (A = W
-// fragment, B = X fragment, both 16-byte reads from LDS).  Wave w covers 64
-// tokens ((w >> 1) quarter) x 128 columns ((w & 1) half: exactly one head
-// block), as 4 x 2 accumulators of 32 x 32.  In the transposed accumulator a
-// lane owns ONE token (lane % 32) and 64 of the head block's 128 columns (the
-// other 64 sit in lane ^ 32), and columns c and c + 64 (a RoPE pair) share a
-// lane, so the norm is a lane-local sum plus one lane-pair exchange and the
-// rotation is register-local.
-//
-// K steps of 64: the x and W tiles (256 rows x 128 B each) pass through
-// registers into a two-stage LDS ring of padded 1 KB blocks (row r in block
-// r % 32, slot r / 32; 16-byte skew between blocks, so the 16 rows of a
-// fragment read land in 16 distinct bank groups).  Each K step is loaded one
-// step ahead, one 16-byte block per lane after every fourth MFMA.
+// Tiling: a workgroup computes a 256-token x 256-column tile as C^T = W X^T
+// with v_mfma_f32_32x32x16_bf16 (A = W fragment, B = X fragment, both 16-byte
+// reads from LDS), in one of two forms:
+//  * eight waves (two per SIMD), each 64 tokens ((w >> 1) quarter) x 128
+//    columns ((w & 1) half), 4 x 2 accumulators of 32 x 32: 6 fragment reads
+//    per 8 MFMAs.  The x and W tiles of a K step (256 rows x 128 B each) pass
+//    through registers into a two-stage LDS ring, one 16-byte block per lane
+//    after every fourth MFMA, each load a whole K step ahead;
+//  * four waves (one per SIMD), each 128 tokens x 128 columns, 4 x 4
+//    accumulators (in AGPRs): 8 fragment reads per 16 MFMAs, so the LDS reads
+//    take a third less.  The tiles go HBM -> LDS directly (global_load_lds_
+//    dwordx4, no staging registers); the barrier that publishes K step kt+1
+//    sits before the last k16 step of K step kt, whose fragments are already in
+//    registers, and the copies of K step kt+2 go out one per two MFMAs, half
+//    after that barrier and half in the first k16 step of K step kt+1, each
+//    with at least two k16 steps to land before the barrier that needs it.
+// The four-wave form is the faster on outputs of 4096 columns and more (the
+// projections and o_proj of the 4096-wide models); on narrower outputs the
+// eight-wave form is, and the launcher picks by the column count (the gated
+// epilogue always takes the eight-wave form).
+// Either way a wave owns exactly one head block of 128 columns, and in the
+// transposed accumulator a lane owns ONE token (lane % 32) and 64 of the
+// block's 128 columns (the other 64 sit in lane ^ 32), and columns c and
+// c + 64 (a RoPE pair) share a lane, so the norm is a lane-local sum plus one
+// lane-pair exchange and the rotation is register-local.  The LDS ring holds
+// padded 1 KB blocks (row r in block r % 32, slot r / 32; 16-byte skew between
+// blocks, so the 16 rows of a fragment read land in 16 distinct bank groups).
 #include <type_traits>
 
 #include "kernels.h"
@@ -46,15 +58,27 @@ constexpr int kBlk = 1040;                 // 1 KB block (8 rows x 128 B) + 16 B
 constexpr int kTile = 32 * kBlk;           // one 256 x 64 operand tile
 constexpr int kStageBytes = 2 * kTile;     // x tile, then W tile
 constexpr int kSmem = 2 * kStageBytes;     // two stages
-constexpr int kThreads = 512;              // 8 waves: two per SIMD
 // qkv: after the ring, the key norm scale (up to 256 floats) and the RoPE
 // frequencies (64 doubles), read per lane in the epilogue; gated qkv: then the
-// halves of the keys' sums of squares ([4 token quarters][2][32 tokens][2 halves]).
+// halves of the keys' sums of squares ([8 token blocks of 32][32 tokens][2 halves]).
 constexpr int kGammaOff = kSmem, kFreqOff = kSmem + 1024, kSsOff = kSmem + 1536, kSmemQkv = kSmem + 1536 + 2048;
 static_assert(kSmemQkv <= 160 * 1024, "LDS per workgroup");
 
 __device__ __forceinline__ bf16x8 lds_load_b128(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes, read from
+// gbase + voff, land at LDS address lds_base + 16 l (M0 holds the wave-uniform
+// base; one wait state after writing M0).  Inline assembly, so the compiler
+// does not wait for every outstanding copy before each LDS read: the K loop
+// waits for its own copies (s_waitcnt vmcnt) before the barrier that
+// publishes a K step.
+__device__ __forceinline__ void load_lds16_async(uint32_t lds_base, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(gbase)
+               : "memory", "m0");
 }
 
 // Sequence and position of packed token n: last s with cu[s] <= n.
@@ -68,12 +92,16 @@ __device__ __forceinline__ void token_position(const GemmArgs& a, int64_t n, int
   pos = (int)(n - a.cu[s]) + (a.start_pos ? a.start_pos[s] : 0);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
+// WAVES: 8 (64 tokens x 128 columns per wave) or 4 (128 x 128).
+template <int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kTB = WAVES == 8 ? 2 : 4;  // token blocks of 32 per wave
+  constexpr int kWT = 32 * kTB;            // tokens per wave
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   lds_u8* lds = (lds_u8*)(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wt = w >> 1, wc = w & 1;  // token quarter (64 tokens), column half (128 columns)
+  const int wt = w >> 1, wc = w & 1;  // token part (kWT tokens), column half (128 columns)
   const int n = lane & 31, hg = lane >> 5;
 
   // Tile order, XCD-aware.  Workgroups are dealt round-robin to the 8 XCDs
@@ -103,116 +131,200 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   const int64_t xrow = a.ldx * 2, wrow = a.ldw * 2;  // bytes per row
   const int last_x = (int)min((int64_t)kBM - 1, a.M - 1 - row0);
   const int last_w = min(kBN - 1, a.N - 1 - col0);
-  // Staging: wave w moves blocks 4w .. 4w+3 of both tiles; lane l carries
-  // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- so its LDS
-  // address inside a block is 16 l.  Rows past the matrix repeat its last row
-  // (their results are never stored).
-  uint32_t xo[4], wo[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int r = w * 4 + m + 32 * (lane >> 3);
-    xo[m] = (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16;
-    wo[m] = (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16;
-  }
-  u32x4 stg[8];  // one K step in flight: x blocks (0..3), then W blocks (4..7)
-  auto gload = [&](int kt, int m) __attribute__((always_inline)) {
-    const char* p = (m < 4 ? xbase + xo[m] : wbase + wo[m - 4]) + (int64_t)kt * kBK * 2;
-    stg[m] = *reinterpret_cast<const u32x4*>(p);
-  };
-  auto lwrite = [&](int kt, int m) __attribute__((always_inline)) {
-    lds_u8* base = lds + (kt & 1) * kStageBytes + (m < 4 ? 0 : kTile) + (w * 4 + (m & 3)) * kBlk + lane * 16;
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base) = stg[m];
-  };
-
-  f32x16 acc[4][2];  // [column block jc][token block it]
+  f32x16 acc[4][kTB];  // [column block jc][token block it]
 #pragma unroll
   for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int it = 0; it < kTB; ++it)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[jc][it][j] = 0.f;
 
   // Fragment (k16 step s): tile row r -> block r % 32, slot r / 32; 16-byte
-  // chunk 2s + hg.  Token block it of the wave: row 64 wt + 32 it + n (slot
-  // 2 wt + it); column block jc: row 128 wc + 32 jc + n (slot 4 wc + jc).
-  const int xoff = n * kBlk + hg * 16 + wt * 256;
+  // chunk 2s + hg.  Token block it of the wave: row kWT wt + 32 it + n (slot
+  // kTB wt + it); column block jc: row 128 wc + 32 jc + n (slot 4 wc + jc).
+  const int xoff = n * kBlk + hg * 16 + wt * kTB * 128;
   const int woff = n * kBlk + hg * 16 + wc * 512;
   const int nk = a.K / kBK;
   float* gk_lds = (float*)(smem + kGammaOff);
   double* w_lds = (double*)(smem + kFreqOff);
   if constexpr (EPI == kGemmQkv) {  // published by the first barrier below
     if (tid < 128) gk_lds[tid] = bf16_to_f32(a.k_gamma[tid]);
-    else if (tid < 192) w_lds[tid - 128] = a.rope.w[tid - 128];
+    if (tid < 64) w_lds[tid] = a.rope.w[tid];
   } else if constexpr (EPI >= kGemmQkvGated) {
     if (tid < 256) gk_lds[tid] = a.gamma_offset + bf16_to_f32(a.k_gamma[tid]);
-    else if (tid < 320) w_lds[tid - 256] = a.rope.w[tid - 256];
+    if (tid < 64) w_lds[tid] = a.rope.w[tid];
   }
-  // K step 0 into LDS stage 0; K step 1 into the staging registers.
-#pragma unroll
-  for (int m = 0; m < 8; ++m) gload(0, m);
-#pragma unroll
-  for (int m = 0; m < 8; ++m) lwrite(0, m);
-  if (nk > 1)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) gload(1, m);
-  bf16x8 wf[2][4], xf[2][2];
+  bf16x8 wf[2][4], xf[2][kTB];
   auto read = [&](int kt, int s, int r) __attribute__((always_inline)) {
-    // order: W 0, x 0, x 1, W 1..3 -- the first MFMAs of a step need W 0 and x 0, 1
+    // order: W 0, x 0 .. kTB-1, W 1..3 -- the first MFMAs of a step need W 0 and every x
     const lds_u8* xs = lds + (kt & 1) * kStageBytes;
     const lds_u8* ws = xs + kTile;
     const int buf = s & 1;
     if (r == 0) wf[buf][0] = lds_load_b128(ws + woff + s * 32);
-    else if (r < 3) xf[buf][r - 1] = lds_load_b128(xs + xoff + (r - 1) * 128 + s * 32);
-    else wf[buf][r - 2] = lds_load_b128(ws + woff + (r - 2) * 128 + s * 32);
+    else if (r <= kTB) xf[buf][r - 1] = lds_load_b128(xs + xoff + (r - 1) * 128 + s * 32);
+    else wf[buf][r - kTB] = lds_load_b128(ws + woff + (r - kTB) * 128 + s * 32);
   };
-  // One K step: kMore / kMore2 say whether K steps kt+1 / kt+2 exist
-  // (compile-time in the steady state, so the MFMA stream has no branches).
-  auto step = [&](int kt, auto more_tag, auto more2_tag) __attribute__((always_inline)) {
-    constexpr bool kMore = decltype(more_tag)::value, kMore2 = decltype(more2_tag)::value;
-    // Step kt is in LDS (every wave's writes done and published); the other
-    // stage, which held step kt-1, is free for step kt+1.
+  constexpr int kReads = 4 + kTB;  // fragment reads per k16 step
+
+  if constexpr (WAVES == 8) {
+    // Staging: wave w moves blocks 4w .. 4w+3 of both tiles; lane l carries
+    // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- so its LDS
+    // address inside a block is 16 l.  Rows past the matrix repeat its last row
+    // (their results are never stored).
+    uint32_t xo[4], wo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = w * 4 + m + 32 * (lane >> 3);
+      xo[m] = (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16;
+      wo[m] = (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16;
+    }
+    u32x4 stg[8];  // one K step in flight: x blocks (0..3), then W blocks (4..7)
+    auto gload = [&](int kt, int m) __attribute__((always_inline)) {
+      const char* p = (m < 4 ? xbase + xo[m] : wbase + wo[m - 4]) + (int64_t)kt * kBK * 2;
+      stg[m] = *reinterpret_cast<const u32x4*>(p);
+    };
+    auto lwrite = [&](int kt, int m) __attribute__((always_inline)) {
+      lds_u8* base = lds + (kt & 1) * kStageBytes + (m < 4 ? 0 : kTile) + (w * 4 + (m & 3)) * kBlk + lane * 16;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base) = stg[m];
+    };
+    // K step 0 into LDS stage 0; K step 1 into the staging registers.
+#pragma unroll
+    for (int m = 0; m < 8; ++m) gload(0, m);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) lwrite(0, m);
+    if (nk > 1)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) gload(1, m);
+    // One K step: kMore / kMore2 say whether K steps kt+1 / kt+2 exist
+    // (compile-time in the steady state, so the MFMA stream has no branches).
+    auto step = [&](int kt, auto more_tag, auto more2_tag) __attribute__((always_inline)) {
+      constexpr bool kMore = decltype(more_tag)::value, kMore2 = decltype(more2_tag)::value;
+      // Step kt is in LDS (every wave's writes done and published); the other
+      // stage, which held step kt-1, is free for step kt+1.
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < kReads; ++r) read(kt, 0, r);
+      // Four k16 steps of 8 MFMAs.  The 6 fragments of step s+1 are read during
+      // step s; after every fourth MFMA one staged block of K step kt+1 goes to
+      // LDS and its register is refilled with the same block of K step kt+2, so
+      // each load has a whole K step to land.  sched_barrier keeps that order;
+      // the two waves of a SIMD interleave their streams.
+#pragma unroll
+      for (int s = 0; s < kBK / 16; ++s) {
+        const int buf = s & 1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int jc = i >> 1, it = i & 1;
+          acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][jc], xf[buf][it], acc[jc][it], 0, 0, 0);
+          if (s + 1 < kBK / 16 && i < kReads) read(kt, s + 1, i);
+          if ((i & 3) == 3) {
+            const int m = 2 * s + (i >> 2);
+            if constexpr (kMore) lwrite(kt + 1, m);
+            if constexpr (kMore2) gload(kt + 2, m);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
+    if (kt + 1 < nk) step(kt++, std::true_type{}, std::false_type{});
+    if (kt < nk) step(kt, std::false_type{}, std::false_type{});
+  } else {
+    // Copies: wave w fills blocks 8w .. 8w+7 of both tiles; lane l carries
+    // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- its LDS
+    // address inside the block is 16 l.  Rows past the matrix repeat its last
+    // row (their results are never stored).
+    uint32_t xo[8], wo[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int r = w * 8 + m + 32 * (lane >> 3);
+      xo[m] = (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16;
+      wo[m] = (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16;
+    }
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    // copy m (0 .. 15) of K step kt: x block 8w + m (m < 8), then W block 8w + m - 8
+    auto copy = [&](int kt, int m) __attribute__((always_inline)) {
+      const uint32_t dst = lds0 + (kt & 1) * kStageBytes + (m < 8 ? 0 : kTile) + (wu * 8 + (m & 7)) * kBlk;
+      const char* src = (m < 8 ? xbase : wbase) + (int64_t)kt * kBK * 2;
+      load_lds16_async(dst, src, m < 8 ? xo[m] : wo[m - 8]);
+    };
+    // K step 0 and the first half of K step 1 (the second half goes out
+    // during K step 0); wait for step 0.
+#pragma unroll
+    for (int m = 0; m < 16; ++m) copy(0, m);
+    if (nk > 1) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) copy(1, m);
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 6; ++r) read(kt, 0, r);
-    // Four k16 steps of 8 MFMAs.  The 6 fragments of step s+1 are read during
-    // step s; after every fourth MFMA one staged block of K step kt+1 goes to
-    // LDS and its register is refilled with the same block of K step kt+2, so
-    // each load has a whole K step to land.  sched_barrier keeps that order;
-    // the two waves of a SIMD interleave their streams.
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
+    for (int r = 0; r < kReads; ++r) read(0, 0, r);
+    // The 16 MFMAs of k16 step s, each followed by fn(i); sched_barrier keeps
+    // the order, so every read and copy has the MFMAs after it to land.
+    auto mfmas = [&](int s, auto fn) __attribute__((always_inline)) {
       const int buf = s & 1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int jc = i >> 1, it = i & 1;
+      for (int i = 0; i < 16; ++i) {
+        const int jc = i >> 2, it = i & 3;
         acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][jc], xf[buf][it], acc[jc][it], 0, 0, 0);
-        if (s + 1 < kBK / 16 && i < 6) read(kt, s + 1, i);
-        if ((i & 3) == 3) {
-          const int m = 2 * s + (i >> 2);
-          if constexpr (kMore) lwrite(kt + 1, m);
-          if constexpr (kMore2) gload(kt + 2, m);
-        }
+        fn(i);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  };
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
-  if (kt + 1 < nk) step(kt++, std::true_type{}, std::false_type{});
-  if (kt < nk) step(kt, std::false_type{}, std::false_type{});
+    };
+    // One K step; kMore / kMore2 say whether K steps kt+1 / kt+2 exist
+    // (compile-time in the steady state, so the MFMA stream has no branches).
+    auto step = [&](int kt, auto more_tag, auto more2_tag) __attribute__((always_inline)) {
+      constexpr bool kMore = decltype(more_tag)::value, kMore2 = decltype(more2_tag)::value;
+      // k16 steps 0..2; the 8 fragments of step s+1 are read during step s, and
+      // k16 step 0 sends the second half of K step kt+1's copies.
+      mfmas(0, [&](int i) __attribute__((always_inline)) {
+        if (i < 8) read(kt, 1, i);
+        if constexpr (kMore)
+          if ((i & 1) == 0) copy(kt + 1, 8 + (i >> 1));
+      });
+#pragma unroll
+      for (int s = 1; s < 3; ++s)
+        mfmas(s, [&](int i) __attribute__((always_inline)) {
+          if (i < 8) read(kt, s + 1, i);
+        });
+      if constexpr (kMore) {
+        // This wave's copies of K step kt+1 have landed; the barrier publishes
+        // everyone's and (its fragment reads done) frees stage kt & 1.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+      }
+      // k16 step 3 from registers; meanwhile the first fragments of K step
+      // kt+1 and the first half of K step kt+2's copies into the freed stage.
+      mfmas(3, [&](int i) __attribute__((always_inline)) {
+        if constexpr (kMore)
+          if (i < 8) read(kt + 1, 0, i);
+        if constexpr (kMore2)
+          if ((i & 1) == 0) copy(kt + 2, i >> 1);
+      });
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
+    if (kt + 1 < nk) step(kt++, std::true_type{}, std::false_type{});
+    step(kt, std::false_type{}, std::false_type{});
+  }
 
-  // ---- epilogue.  acc[jc][it][j]: token row0 + 64 wt + 32 it + n, column
+  // ---- epilogue.  acc[jc][it][j]: token row0 + kWT wt + 32 it + n, column
   // col0 + 128 wc + 32 jc + 8 (j / 4) + 4 hg + j % 4.
   const int ccol = col0 + 128 * wc;  // the wave's first column (a head block in the qkv form)
   // The gated q/k/v epilogue (head_dim 256).  Column regions -- tiles never
   // straddle them, every width being a multiple of 256 -- are: Hq query rows of
   // q_width values, written raw to q_out [M][Hq][q_width]; Hkv key heads, normed
   // and partially rotated at each token's position; Hkv value heads.  A head of
-  // 256 spans the tile: wave (wt, wc) holds dims 128 wc .. 128 wc + 127 of its 64
+  // 256 spans the tile: wave (wt, wc) holds dims 128 wc .. 128 wc + 127 of its kWT
   // tokens, so a key's sum of squares adds the two waves' halves through LDS (the
   // branch is uniform over the workgroup, so its barrier is too), and the
   // rotated dims (at most 128) all lie in the waves with wc = 0.  acc[jc][it][j]:
-  // token row0 + 64 wt + 32 it + n, column 32 jc + 8 (j / 4) + 4 hg + j % 4 of the
+  // token row0 + kWT wt + 32 it + n, column 32 jc + 8 (j / 4) + 4 hg + j % 4 of the
   // wave's 128.
   if constexpr (EPI >= kGemmQkvGated) {
     // one instantiation per rotary width: 32, 64 or 128 leading dims turn
@@ -228,8 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
     const int qcols = a.Hq * a.q_width;
     if (col0 < qcols) {  // query (and gate) values, raw
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int64_t tok = row0 + 64 * wt + 32 * it + n;
+      for (int it = 0; it < kTB; ++it) {
+        const int64_t tok = row0 + kWT * wt + 32 * it + n;
         if (tok >= a.M) continue;
         float x[4][16];
 #pragma unroll
@@ -243,29 +355,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
     constexpr int D = kMaxD;
     const bool is_k = col0 < qcols + a.Hkv * D;
     const int kv = (col0 - qcols) / D - (is_k ? 0 : a.Hkv);
-    float inv[2] = {0.f, 0.f};
+    float inv[kTB] = {};
     if (is_k) {
       float* ss_lds = (float*)(smem + kSsOff);
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
+      for (int it = 0; it < kTB; ++it) {
         float ss = 0.f;
 #pragma unroll
         for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
           for (int j = 0; j < 16; ++j) ss += acc[jc][it][j] * acc[jc][it][j];
         ss = pair_sum(ss);  // lane n ^ 32 holds the other 64 of the wave's 128 dims
-        if (hg == 0) ss_lds[((wt * 2 + it) * 32 + n) * 2 + wc] = ss;
+        if (hg == 0) ss_lds[((wt * kTB + it) * 32 + n) * 2 + wc] = ss;
       }
       __syncthreads();
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const float* p = ss_lds + ((wt * 2 + it) * 32 + n) * 2;
+      for (int it = 0; it < kTB; ++it) {
+        const float* p = ss_lds + ((wt * kTB + it) * 32 + n) * 2;
         inv[it] = rsqrtf((p[0] + p[1]) * (1.0f / D) + a.eps);
       }
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t tok = row0 + 64 * wt + 32 * it + n;
+    for (int it = 0; it < kTB; ++it) {
+      const int64_t tok = row0 + kWT * wt + 32 * it + n;
       const bool valid = tok < a.M;
       float x[4][16];
 #pragma unroll
@@ -323,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   if (ccol >= a.N) return;
   if constexpr (EPI == kGemmPlain) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t tok = row0 + 64 * wt + 32 * it + n;
+    for (int it = 0; it < kTB; ++it) {
+      const int64_t tok = row0 + kWT * wt + 32 * it + n;
       if (tok >= a.M) continue;
       uint16_t* dst = a.y + tok * a.ldy + ccol + 4 * hg;
 #pragma unroll
@@ -342,8 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
     // norm scale of column 32 jc + 8 (j / 4) + 4 hg + j % 4
     auto gk = [&](int jc, int j) __attribute__((always_inline)) { return gk_lds[32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)]; };
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t tok = row0 + 64 * wt + 32 * it + n;
+    for (int it = 0; it < kTB; ++it) {
+      const int64_t tok = row0 + kWT * wt + 32 * it + n;
       const bool valid = tok < a.M;
       float x[4][16];
 #pragma unroll
@@ -411,14 +523,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs a) {
   }
 }
 
-template <int EPI>
-hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+template <int EPI, int WAVES>
+hipError_t launch_w(const GemmArgs& a, hipStream_t st) {
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)k_gemm<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemQkv);
+      hipFuncSetAttribute((const void*)k_gemm<EPI, WAVES>, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemQkv);
   if (attr != hipSuccess) return attr;
   const int64_t tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_gemm<EPI>, dim3((unsigned)tiles), dim3(kThreads), kSmemQkv, st, a);
+  hipLaunchKernelGGL((k_gemm<EPI, WAVES>), dim3((unsigned)tiles), dim3(WAVES * 64), kSmemQkv, st, a);
   return hipGetLastError();
+}
+
+// The four-wave form on outputs of 4096 columns and more, the eight-wave form
+// below (measured: on 2048-column outputs the four-wave form lost 7-8%).  The
+// gated epilogue always takes the eight-wave form: with 4 x 4 accumulators
+// live it would spill, and the two forms measured the same on it.
+template <int EPI>
+hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+  if constexpr (EPI >= kGemmQkvGated) return launch_w<EPI, 8>(a, st);
+  else return a.N >= 4096 ? launch_w<EPI, 4>(a, st) : launch_w<EPI, 8>(a, st);
 }
 
 }  // namespace

@@ -39,8 +39,12 @@ def linear_bound(x, w, k):
     return y, 2.0 ** -8 * np.abs(y) + k * 2.0 ** -23 * mag
 
 
+# n >= 4096 takes the four-wave tile form (one, two and an odd number of K
+# steps; a ragged last column tile; the q/k/v width of Qwen3-8B), n < 4096 the
+# eight-wave form.
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (255, 384, 128), (257, 256, 1024), (1000, 640, 320),
-                                   (4096, 1024, 4096)])
+                                   (4096, 1024, 4096), (1, 4096, 64), (257, 4224, 128), (1000, 4096, 320),
+                                   (300, 6144, 4096)])
 def test_linear(m, n, k):
     rng = np.random.default_rng(m + n + k)
     x = inputs.round_to_bf16(rng.standard_normal((m, k)).astype(np.float32))
