@@ -109,27 +109,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
   // of them at once (one per CU).  The tile grid is cut into 8 regions, one
   // per XCD, so an XCD streams only its region's panels of x and W.  Where the
   // region divides into blocks of 32 tiles (4 token tiles x 8 column tiles, or
-  // 8 x 4), the four-wave form walks it block by block: the 32 workgroups an
-  // XCD runs together then read 12 panels (4 + 8) for their 32 tiles, the
-  // fewest any shape allows.  Otherwise the region is walked row by row
-  // (the eight-wave form always: there the block walk measured slower on the
-  // gated q/k/v projection, whose last block column is all key and value
-  // heads); failing even that, consecutive workgroups take consecutive
-  // column tiles.
+  // 8 x 4), it is walked block by block: the 32 workgroups an XCD runs
+  // together then read 12 panels (4 + 8) for their 32 tiles, the fewest any
+  // shape allows.  With 8 x 1 regions every XCD covers every column block, so
+  // XCD x starts at column block x: the key and value heads of a q/k/v
+  // projection (its last columns, whose epilogue is the heaviest) are then
+  // spread over the launch instead of falling on every CU at once.  Otherwise
+  // the region is walked row by row; failing even that, consecutive
+  // workgroups take consecutive column tiles.
   const int tiles_n = (a.N + kBN - 1) / kBN;
   const int tiles_m = (int)((a.M + kBM - 1) / kBM);
   int tm, tn;
   const int x = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  if (WAVES == 4 && tiles_m % 16 == 0 && tiles_n % 16 == 0) {
+  if (tiles_m % 16 == 0 && tiles_n % 16 == 0) {
     // regions: 4 x 2 (a quarter of the token tiles, half of the column tiles); blocks 4 x 8
     const int rm = tiles_m / 4, rn = tiles_n / 2, blk = idx >> 5, in = idx & 31, bpr = rn / 8;
     tm = (x >> 1) * rm + (blk / bpr) * 4 + (in >> 3);
     tn = (x & 1) * rn + (blk % bpr) * 8 + (in & 7);
-  } else if (WAVES == 4 && tiles_m % 64 == 0 && tiles_n % 4 == 0) {
+  } else if (tiles_m % 64 == 0 && tiles_n % 4 == 0) {
     // regions: 8 x 1 (an eighth of the token tiles, every column tile); blocks 8 x 4
     const int rm = tiles_m / 8, blk = idx >> 5, in = idx & 31, bpr = tiles_n / 4;
     tm = x * rm + (blk / bpr) * 8 + (in >> 2);
-    tn = (blk % bpr) * 4 + (in & 3);
+    tn = ((blk % bpr + x) % bpr) * 4 + (in & 3);
   } else if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
     const int rn = tiles_n / 2;
     tm = (x >> 1) * (tiles_m / 4) + idx / rn;
