@@ -309,13 +309,14 @@ def measure_append(dev, n_calls=20, new_tokens=512):
     flops = accounting.append_flops(split, [new_tokens] * spec.n_seq, spec.n_q_heads)
     k_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in kev]))
     c_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
-    return {"metric": "append attention TFLOP/s", "unit": "TFLOP/s",
-            "workload": f"qwen3-8b-append-bf16 {spec.n_seq}x({split[0]} cached + {new_tokens} new) Hq{spec.n_q_heads} Hkv{spec.n_kv_heads}",
+    workload = f"qwen3-8b-append-bf16 {spec.n_seq}x({split[0]} cached + {new_tokens} new) Hq{spec.n_q_heads} Hkv{spec.n_kv_heads}"
+    return {"metric": "append attention TFLOP/s", "unit": "TFLOP/s", "workload": workload,
             "value": round(flops / (c_ms * 1e-3) / 1e12, 2), "call_ms": round(c_ms, 4),
             "roofline": {"kernel": "k_prefill_bf16", "bound": "mfma", "achieved": round(flops / (k_ms * 1e-3) / 1e12, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops / (k_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops}}
+                         "kernel_ms": round(k_ms, 4), "algorithmic_flops": flops,
+                         "traffic": recorded_traffic("k_prefill_bf16", "k_prefill.hip", workload)}}
 
 
 def measure_gated(dev, n_calls=20):
