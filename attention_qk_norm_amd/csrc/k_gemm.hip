@@ -448,22 +448,37 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
 
     return;
   }
-  if (ccol >= a.N) return;
   if constexpr (EPI == kGemmPlain) {
+    // The tile leaves as whole rows: the accumulators go to LDS as bf16 (the
+    // ring is idle once every wave is past its last K step), then each wave
+    // stores two rows of 512 B per instruction.  Straight from the
+    // accumulators, each store instruction touched 32 rows 16 B apart.  Row r
+    // holds its 16-byte chunk c (columns 8c .. 8c+7) at position c ^ (r % 16),
+    // so the full-row reads are conflict-free.
+    auto slot = [](int r, int c) __attribute__((always_inline)) { return r * 512 + ((c ^ (r & 15)) << 4); };
+    __syncthreads();  // every wave's last fragment reads are done
 #pragma unroll
     for (int it = 0; it < kTB; ++it) {
-      const int64_t tok = row0 + kWT * wt + 32 * it + n;
-      if (tok >= a.M) continue;
-      uint16_t* dst = a.y + tok * a.ldy + ccol + 4 * hg;
+      const int r = kWT * wt + 32 * it + n;
 #pragma unroll
       for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
         for (int jg = 0; jg < 4; ++jg)
-          *reinterpret_cast<u32x2*>(dst + 32 * jc + 8 * jg) =
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + slot(r, 16 * wc + 4 * jc + jg) + 8 * hg) =
               u32x2{pack_bf16x2(acc[jc][it][4 * jg], acc[jc][it][4 * jg + 1]),
                     pack_bf16x2(acc[jc][it][4 * jg + 2], acc[jc][it][4 * jg + 3])};
     }
+    __syncthreads();
+    const int rows = (int)min((int64_t)kBM, a.M - row0), cols = min(kBN, a.N - col0);
+#pragma unroll
+    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
+      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
+      if (r < rows && 8 * c < cols)
+        *reinterpret_cast<u32x4*>(a.y + (row0 + r) * a.ldy + col0 + 8 * c) =
+            *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+    }
   } else {
+    if (ccol >= a.N) return;
     const int hh = ccol / 128;  // head block: query, key or value head
     const bool is_q = hh < a.Hq, is_k = !is_q && hh < a.Hq + a.Hkv;
     const int kv = is_k ? hh - a.Hq : hh - a.Hq - a.Hkv;

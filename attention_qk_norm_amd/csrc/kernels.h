@@ -135,7 +135,7 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t st);
 // y = x W^T, bf16 operands, fp32 accumulation.  x [M][K] (row stride ldx), W
 // [N][K] (row stride ldw); K a multiple of 64, N a multiple of 128.
 enum GemmEpilogue : int {
-  kGemmPlain = 0,     // y [M][N] (row stride ldy), rounded to bf16
+  kGemmPlain = 0,     // y [M][N] (row stride ldy, a multiple of 8), rounded to bf16
   kGemmQkv = 1,       // columns = Hq query, Hkv key, Hkv value head blocks of 128
   kGemmQkvGated = 2,  // columns = Hq query rows of q_width (query, then gate), Hkv key and Hkv
                       // value heads of 256 (the gated layers)
