@@ -478,27 +478,35 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
             *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
     }
   } else {
-    if (ccol >= a.N) return;
-    const int hh = ccol / 128;  // head block: query, key or value head
+    // The two column halves of the tile are head blocks: query, key or value.
+    // Keys are normed and rotated here from the fp32 accumulators; then, as in
+    // the plain tile, the rows are staged in LDS and leave whole: each 256-byte
+    // head row to q_out (query) or to the token's cache slot (key, value).  The
+    // (sequence, position) of every token goes through LDS from the wave that
+    // looked it up: the tile's last column half, a key or value block whenever
+    // either half is.
+    auto slot = [](int r, int c) __attribute__((always_inline)) { return r * 512 + ((c ^ (r & 15)) << 4); };
+    typedef __attribute__((address_space(3))) int32_t lds_i32;
+    lds_i32* meta = (lds_i32*)(lds + kSsOff);  // [256][2]: sequence, position
+    const bool half_ok = ccol < a.N;
+    const int hh = ccol / 128;  // this wave's head block
     const bool is_q = hh < a.Hq, is_k = !is_q && hh < a.Hq + a.Hkv;
-    const int kv = is_k ? hh - a.Hq : hh - a.Hq - a.Hkv;
+    const bool publisher = !is_q && (wc == 1 || col0 + 128 >= a.N);
     // norm scale of column 32 jc + 8 (j / 4) + 4 hg + j % 4
     auto gk = [&](int jc, int j) __attribute__((always_inline)) { return gk_lds[32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)]; };
+    __syncthreads();  // every wave's last fragment reads are done
 #pragma unroll
     for (int it = 0; it < kTB; ++it) {
-      const int64_t tok = row0 + kWT * wt + 32 * it + n;
-      const bool valid = tok < a.M;
+      const int r = kWT * wt + 32 * it + n;
+      const int64_t tok = row0 + r;
       float x[4][16];
 #pragma unroll
       for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[jc][j] = acc[jc][it][j];
-      uint16_t* dst;
-      if (is_q) {
-        dst = a.q_out + (tok * a.Hq + hh) * 128;
-      } else {
-        int s = 0, pos = 0;
-        if (valid) token_position(a, tok, s, pos);
+      int s = 0, pos = 0;
+      if (!is_q && half_ok) {
+        if (tok < a.M) token_position(a, tok, s, pos);
         if (is_k) {
           // QK-Norm from the fp32 accumulators; RMS is rotation-invariant, so
           // one inv serves both orders, which differ in whether the norm scale
@@ -524,8 +532,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
             for (int j = 0; j < 16; ++j) {
               const double wfreq = w_lds[32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)];
               const double t = (double)pos * (wfreq * 0.15915494309189535);
-              const float r = (float)(t - rint(t));
-              const float c = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
+              const float rr = (float)(t - rint(t));
+              const float c = __builtin_amdgcn_cosf(rr), sn = __builtin_amdgcn_sinf(rr);
               const float y1 = x[jc][j], y2 = x[jc + 2][j];
               x[jc][j] = y1 * c - y2 * sn;
               x[jc + 2][j] = y2 * c + y1 * sn;
@@ -536,20 +544,39 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
 #pragma unroll
               for (int j = 0; j < 16; ++j) x[jc][j] *= inv * gk(jc, j);
         }
-        uint16_t* cache = is_k ? a.k_cache : a.v_cache;
-        if (cache)
-          dst = cache + s * a.cs_seq + kv * a.cs_head + (int64_t)pos * a.cs_tok;
-        else
-          dst = (is_k ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * 128;
       }
-      if (!valid) continue;
-      dst += 4 * hg;
+      if (publisher && hg == 0) {
+        meta[2 * r] = s;
+        meta[2 * r + 1] = pos;
+      }
+      if (half_ok)
 #pragma unroll
-      for (int jc = 0; jc < 4; ++jc)
+        for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg)
-          *reinterpret_cast<u32x2*>(dst + 32 * jc + 8 * jg) =
-              u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
+          for (int jg = 0; jg < 4; ++jg)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + slot(r, 16 * wc + 4 * jc + jg) + 8 * hg) =
+                u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
+      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
+      const int64_t tok = row0 + r;
+      const int col = col0 + 128 * (c >> 4);
+      if (tok >= a.M || col >= a.N) continue;
+      const int hb = col / 128;
+      uint16_t* dst;
+      if (hb < a.Hq) {
+        dst = a.q_out + (tok * a.Hq + hb) * 128;
+      } else {
+        const bool k_blk = hb < a.Hq + a.Hkv;
+        const int kv = k_blk ? hb - a.Hq : hb - a.Hq - a.Hkv;
+        uint16_t* cache = k_blk ? a.k_cache : a.v_cache;
+        dst = cache ? cache + meta[2 * r] * a.cs_seq + kv * a.cs_head + (int64_t)meta[2 * r + 1] * a.cs_tok
+                    : (k_blk ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * 128;
+      }
+      *reinterpret_cast<u32x4*>(dst + 8 * (c & 15)) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
     }
   }
 }
