@@ -345,32 +345,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
   if constexpr (EPI >= kGemmQkvGated) {
     // one instantiation per rotary width: 32, 64 or 128 leading dims turn
     constexpr int ROT = EPI == kGemmQkvGated ? 32 : EPI == kGemmQkvGated + 1 ? 64 : 128;
-    auto store128 = [&](uint16_t* dst, const float (&x)[4][16]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int jc = 0; jc < 4; ++jc)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg)
-          *reinterpret_cast<u32x2*>(dst + 32 * jc + 8 * jg) =
-              u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
-    };
+    // As in the other epilogues the finished rows are staged in LDS (row r,
+    // 16-byte chunk c at position c ^ (r % 16)) and leave whole: a query tile is
+    // 512 contiguous bytes of each token's q_out row, a key or value tile one
+    // head of 256 dims, i.e. one cache slot.  The (sequence, position) of each
+    // token sits in the 2 KB of the ring past the staged rows.
+    auto slot = [](int r, int c) __attribute__((always_inline)) { return r * 512 + ((c ^ (r & 15)) << 4); };
+    typedef __attribute__((address_space(3))) int32_t lds_i32;
+    lds_i32* meta = (lds_i32*)(lds + kBM * 512);  // [256][2]: sequence, position
+    static_assert(kBM * 512 + kBM * 8 <= kSmem, "staged rows and positions fit in the ring");
     const int qcols = a.Hq * a.q_width;
-    if (col0 < qcols) {  // query (and gate) values, raw
-#pragma unroll
-      for (int it = 0; it < kTB; ++it) {
-        const int64_t tok = row0 + kWT * wt + 32 * it + n;
-        if (tok >= a.M) continue;
-        float x[4][16];
-#pragma unroll
-        for (int jc = 0; jc < 4; ++jc)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) x[jc][j] = acc[jc][it][j];
-        store128(a.q_out + tok * qcols + col0 + 128 * wc + 4 * hg, x);
-      }
-      return;
-    }
+    const bool q_tile = col0 < qcols;  // query (and gate) values, raw
     constexpr int D = kMaxD;
-    const bool is_k = col0 < qcols + a.Hkv * D;
-    const int kv = (col0 - qcols) / D - (is_k ? 0 : a.Hkv);
+    const bool is_k = !q_tile && col0 < qcols + a.Hkv * D;
+    const int kv = q_tile ? 0 : (col0 - qcols) / D - (is_k ? 0 : a.Hkv);
     float inv[kTB] = {};
     if (is_k) {
       float* ss_lds = (float*)(smem + kSsOff);
@@ -391,61 +379,85 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
         inv[it] = rsqrtf((p[0] + p[1]) * (1.0f / D) + a.eps);
       }
     }
+    __syncthreads();  // every wave's last fragment reads are done
 #pragma unroll
     for (int it = 0; it < kTB; ++it) {
-      const int64_t tok = row0 + kWT * wt + 32 * it + n;
-      const bool valid = tok < a.M;
+      const int r = kWT * wt + 32 * it + n;
+      const int64_t tok = row0 + r;
       float x[4][16];
 #pragma unroll
       for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[jc][j] = acc[jc][it][j];
-      int s = 0, pos = 0;
-      if (valid) token_position(a, tok, s, pos);
-      if (is_k) {
-        // norm scale 1 + w (the table holds gamma_offset + gamma); RMS is
-        // rotation-invariant, so one inv serves both orders
-        auto scale = [&]() __attribute__((always_inline)) {
+      if (!q_tile) {
+        int s = 0, pos = 0;
+        if (tok < a.M) token_position(a, tok, s, pos);
+        if (is_k) {
+          // norm scale 1 + w (the table holds gamma_offset + gamma); RMS is
+          // rotation-invariant, so one inv serves both orders
+          auto scale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int jc = 0; jc < 4; ++jc)
+            for (int jc = 0; jc < 4; ++jc)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) x[jc][j] *= inv[it] * gk_lds[128 * wc + 32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)];
-        };
-        // dims c and c + rot/2 (c < rot/2) turn by pos * w_c, the angle reduced
-        // in fp64 and evaluated by the hardware sine/cosine, which take turns
-        auto turn = [&](int jc1, int j1, int jc2, int j2) __attribute__((always_inline)) {
-          const int c = 32 * jc1 + 8 * (j1 >> 2) + 4 * hg + (j1 & 3);
-          const double t = (double)pos * (w_lds[c] * 0.15915494309189535);
-          const float r = (float)(t - rint(t));
-          const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
-          const float y1 = x[jc1][j1], y2 = x[jc2][j2];
-          x[jc1][j1] = y1 * cs - y2 * sn;
-          x[jc2][j2] = y2 * cs + y1 * sn;
-        };
-        if (a.order == 0) scale();
-        if (wc == 0) {
-          if constexpr (ROT == 128) {
+              for (int j = 0; j < 16; ++j) x[jc][j] *= inv[it] * gk_lds[128 * wc + 32 * jc + 8 * (j >> 2) + 4 * hg + (j & 3)];
+          };
+          // dims c and c + rot/2 (c < rot/2) turn by pos * w_c, the angle reduced
+          // in fp64 and evaluated by the hardware sine/cosine, which take turns
+          auto turn = [&](int jc1, int j1, int jc2, int j2) __attribute__((always_inline)) {
+            const int c = 32 * jc1 + 8 * (j1 >> 2) + 4 * hg + (j1 & 3);
+            const double t = (double)pos * (w_lds[c] * 0.15915494309189535);
+            const float rr = (float)(t - rint(t));
+            const float cs = __builtin_amdgcn_cosf(rr), sn = __builtin_amdgcn_sinf(rr);
+            const float y1 = x[jc1][j1], y2 = x[jc2][j2];
+            x[jc1][j1] = y1 * cs - y2 * sn;
+            x[jc2][j2] = y2 * cs + y1 * sn;
+          };
+          if (a.order == 0) scale();
+          if (wc == 0) {
+            if constexpr (ROT == 128) {
 #pragma unroll
-            for (int jc = 0; jc < 2; ++jc)
+              for (int jc = 0; jc < 2; ++jc)
 #pragma unroll
-              for (int j = 0; j < 16; ++j) turn(jc, j, jc + 2, j);
-          } else if constexpr (ROT == 64) {
+                for (int j = 0; j < 16; ++j) turn(jc, j, jc + 2, j);
+            } else if constexpr (ROT == 64) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) turn(0, j, 1, j);
-          } else {
+              for (int j = 0; j < 16; ++j) turn(0, j, 1, j);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) turn(0, j, 0, j + 8);
+              for (int j = 0; j < 8; ++j) turn(0, j, 0, j + 8);
+            }
           }
+          if (a.order != 0) scale();
         }
-        if (a.order != 0) scale();
+        if (wc == 0 && hg == 0) {
+          meta[2 * r] = s;
+          meta[2 * r + 1] = pos;
+        }
       }
-      if (!valid) continue;
-      uint16_t* cache = is_k ? a.k_cache : a.v_cache;
-      uint16_t* dst = cache ? cache + s * a.cs_seq + kv * a.cs_head + (int64_t)pos * a.cs_tok
-                            : (is_k ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * D;
-      store128(dst + 128 * wc + 4 * hg, x);
+#pragma unroll
+      for (int jc = 0; jc < 4; ++jc)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg)
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(lds + slot(r, 16 * wc + 4 * jc + jg) + 8 * hg) =
+              u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
     }
-
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
+      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
+      const int64_t tok = row0 + r;
+      if (tok >= a.M) continue;
+      uint16_t* dst;
+      if (q_tile) {
+        dst = a.q_out + tok * qcols + col0;
+      } else {
+        uint16_t* cache = is_k ? a.k_cache : a.v_cache;
+        dst = cache ? cache + meta[2 * r] * a.cs_seq + kv * a.cs_head + (int64_t)meta[2 * r + 1] * a.cs_tok
+                    : (is_k ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * D;
+      }
+      *reinterpret_cast<u32x4*>(dst + 8 * c) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+    }
     return;
   }
   if constexpr (EPI == kGemmPlain) {
