@@ -35,10 +35,10 @@
 //    registers, and the copies of K step kt+2 go out one per two MFMAs, half
 //    after that barrier and half in the first k16 step of K step kt+1, each
 //    with at least two k16 steps to land before the barrier that needs it.
-// The four-wave form is the faster on outputs of 4096 columns and more (the
-// projections and o_proj of the 4096-wide models); on narrower outputs the
-// eight-wave form is, and the launcher picks by the column count (the gated
-// epilogue always takes the eight-wave form).
+// The plain and q/k/v epilogues take the four-wave form; the gated epilogue
+// the eight-wave form, where its norm and partial rotation fit without spills.
+// Every epilogue stages the finished tile in LDS (the ring is idle by then) and
+// stores whole rows.
 // Either way a wave owns exactly one head block of 128 columns, and in the
 // transposed accumulator a lane owns ONE token (lane % 32) and 64 of the
 // block's 128 columns (the other 64 sit in lane ^ 32), and columns c and
@@ -603,14 +603,15 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The four-wave form on outputs of 4096 columns and more, the eight-wave form
-// below (measured: on 2048-column outputs the four-wave form lost 7-8%).  The
-// gated epilogue always takes the eight-wave form: with 4 x 4 accumulators
-// live it would spill, and the two forms measured the same on it.
+// The four-wave form for the plain and q/k/v epilogues, at every width (with
+// the tile staged through LDS on its way out it measured 6-11% faster than the
+// eight-wave form from 256 to 3072 columns, and faster above).  The gated
+// epilogue takes the eight-wave form: with 4 x 4 accumulators live its norm and
+// partial rotation spill.
 template <int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI >= kGemmQkvGated) return launch_w<EPI, 8>(a, st);
-  else return a.N >= 4096 ? launch_w<EPI, 4>(a, st) : launch_w<EPI, 8>(a, st);
+  else return launch_w<EPI, 4>(a, st);
 }
 
 }  // namespace

@@ -39,12 +39,13 @@ def linear_bound(x, w, k):
     return y, 2.0 ** -8 * np.abs(y) + k * 2.0 ** -23 * mag
 
 
-# n >= 4096 takes the four-wave tile form (one, two and an odd number of K
-# steps; a ragged last column tile; the q/k/v width of Qwen3-8B), n < 4096 the
-# eight-wave form.  The last five shapes take the XCD block walks over 256 x 256
-# tiles: 4 x 8 blocks in 4 x 2 regions (one and two block columns per region),
-# and 8 x 4 blocks in 8 x 1 regions with the per-XCD column-block rotation
-# (one, three and six block columns), in both forms.
+# Every width takes the four-wave tile form: one, two and an odd number of K
+# steps, ragged last row and column tiles (a column tile of 128), the q/k/v
+# width of Qwen3-8B.  The last five shapes take the XCD block walks over
+# 256 x 256 tiles: 4 x 8 blocks in 4 x 2 regions (one and two block columns per
+# region), and 8 x 4 blocks in 8 x 1 regions with the per-XCD column-block
+# rotation (one, three and six block columns).  The eight-wave form serves the
+# gated q/k/v epilogue, tested with the gated sublayer.
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (255, 384, 128), (257, 256, 1024), (1000, 640, 320),
                                    (4096, 1024, 4096), (1, 4096, 64), (257, 4224, 128), (1000, 4096, 320),
                                    (300, 6144, 4096), (4096, 4096, 64), (4096, 8192, 64), (16384, 1024, 64),
