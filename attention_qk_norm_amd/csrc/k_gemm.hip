@@ -570,25 +570,38 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
                 u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
-      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
-      const int64_t tok = row0 + r;
-      const int col = col0 + 128 * (c >> 4);
-      if (tok >= a.M || col >= a.N) continue;
-      const int hb = col / 128;
-      uint16_t* dst;
+    // A thread keeps one chunk column c (and so one head block) and walks the
+    // rows r0, r0 + kThreads / 32, ...; everything but the row is set up once.
+    constexpr int kRowStep = kThreads / 32;
+    const int c = tid & 31, r0 = tid >> 5;
+    const int hb = (col0 >> 7) + (c >> 4);  // the chunk's head block
+    if (128 * hb < a.N) {
       if (hb < a.Hq) {
-        dst = a.q_out + (tok * a.Hq + hb) * 128;
+        uint16_t* dst = a.q_out + (row0 * a.Hq + hb) * 128 + 8 * (c & 15);
+        const int64_t step = (int64_t)a.Hq * 128;
+#pragma unroll
+        for (int i = 0; i < kBM / kRowStep; ++i) {
+          const int r = r0 + kRowStep * i;
+          if (row0 + r < a.M)
+            *reinterpret_cast<u32x4*>(dst + r * step) =
+                *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+        }
       } else {
         const bool k_blk = hb < a.Hq + a.Hkv;
         const int kv = k_blk ? hb - a.Hq : hb - a.Hq - a.Hkv;
         uint16_t* cache = k_blk ? a.k_cache : a.v_cache;
-        dst = cache ? cache + meta[2 * r] * a.cs_seq + kv * a.cs_head + (int64_t)meta[2 * r + 1] * a.cs_tok
-                    : (k_blk ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * 128;
+        uint16_t* packed = (k_blk ? a.k_out : a.v_out) + (row0 * a.Hkv + kv) * 128 + 8 * (c & 15);
+        uint16_t* slot0 = cache ? cache + kv * a.cs_head + 8 * (c & 15) : nullptr;
+#pragma unroll
+        for (int i = 0; i < kBM / kRowStep; ++i) {
+          const int r = r0 + kRowStep * i;
+          if (row0 + r >= a.M) continue;
+          uint16_t* dst = cache ? slot0 + meta[2 * r] * a.cs_seq + (int64_t)meta[2 * r + 1] * a.cs_tok
+                                : packed + (int64_t)r * a.Hkv * 128;
+          *reinterpret_cast<u32x4*>(dst) =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+        }
       }
-      *reinterpret_cast<u32x4*>(dst + 8 * (c & 15)) =
-          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
     }
   }
 }
