@@ -442,20 +442,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
               u32x2{pack_bf16x2(x[jc][4 * jg], x[jc][4 * jg + 1]), pack_bf16x2(x[jc][4 * jg + 2], x[jc][4 * jg + 3])};
     }
     __syncthreads();
+    // A thread keeps one chunk column c and walks the rows r0, r0 + kThreads / 32, ...
+    constexpr int kRowStep = kThreads / 32;
+    const int c = tid & 31, r0 = tid >> 5;
+    uint16_t* cache = is_k ? a.k_cache : a.v_cache;
+    uint16_t* base = q_tile ? a.q_out + row0 * qcols + col0 + 8 * c
+                            : (cache ? cache + kv * a.cs_head : (is_k ? a.k_out : a.v_out) + (row0 * a.Hkv + kv) * D) + 8 * c;
+    const int64_t step = q_tile ? (int64_t)qcols : (int64_t)a.Hkv * D;  // per row, without a cache
 #pragma unroll
-    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
-      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
-      const int64_t tok = row0 + r;
-      if (tok >= a.M) continue;
-      uint16_t* dst;
-      if (q_tile) {
-        dst = a.q_out + tok * qcols + col0;
-      } else {
-        uint16_t* cache = is_k ? a.k_cache : a.v_cache;
-        dst = cache ? cache + meta[2 * r] * a.cs_seq + kv * a.cs_head + (int64_t)meta[2 * r + 1] * a.cs_tok
-                    : (is_k ? a.k_out : a.v_out) + (tok * a.Hkv + kv) * D;
-      }
-      *reinterpret_cast<u32x4*>(dst + 8 * c) =
+    for (int i = 0; i < kBM / kRowStep; ++i) {
+      const int r = r0 + kRowStep * i;
+      if (row0 + r >= a.M) continue;
+      uint16_t* dst = (q_tile || !cache) ? base + r * step
+                                         : base + meta[2 * r] * a.cs_seq + (int64_t)meta[2 * r + 1] * a.cs_tok;
+      *reinterpret_cast<u32x4*>(dst) =
           *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
     }
     return;
@@ -481,13 +481,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
                     pack_bf16x2(acc[jc][it][4 * jg + 2], acc[jc][it][4 * jg + 3])};
     }
     __syncthreads();
-    const int rows = (int)min((int64_t)kBM, a.M - row0), cols = min(kBN, a.N - col0);
+    // A thread keeps one chunk column c and walks the rows r0, r0 + kThreads / 32, ...
+    constexpr int kRowStep = kThreads / 32;
+    const int rows = (int)min((int64_t)kBM, a.M - row0), c = tid & 31, r0 = tid >> 5;
+    if (8 * c < a.N - col0) {
+      uint16_t* dst = a.y + row0 * a.ldy + col0 + 8 * c;
 #pragma unroll
-    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
-      const int id = tid + kThreads * i, r = id >> 5, c = id & 31;
-      if (r < rows && 8 * c < cols)
-        *reinterpret_cast<u32x4*>(a.y + (row0 + r) * a.ldy + col0 + 8 * c) =
-            *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+      for (int i = 0; i < kBM / kRowStep; ++i) {
+        const int r = r0 + kRowStep * i;
+        if (r < rows)
+          *reinterpret_cast<u32x4*>(dst + r * a.ldy) =
+              *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lds + slot(r, c));
+      }
     }
   } else {
     // The two column halves of the tile are head blocks: query, key or value.
