@@ -24,21 +24,19 @@
 // reads from LDS), in one of two forms:
 //  * eight waves (two per SIMD), each 64 tokens ((w >> 1) quarter) x 128
 //    columns ((w & 1) half), 4 x 2 accumulators of 32 x 32: 6 fragment reads
-//    per 8 MFMAs.  The x and W tiles of a K step (256 rows x 128 B each) pass
-//    through registers into a two-stage LDS ring, one 16-byte block per lane
-//    after every fourth MFMA, each load a whole K step ahead;
+//    per 8 MFMAs;
 //  * four waves (one per SIMD), each 128 tokens x 128 columns, 4 x 4
 //    accumulators (in AGPRs): 8 fragment reads per 16 MFMAs, so the LDS reads
-//    take a third less.  The tiles go HBM -> LDS directly (global_load_lds_
-//    dwordx4, no staging registers); the barrier that publishes K step kt+1
-//    sits before the last k16 step of K step kt, whose fragments are already in
-//    registers, and the copies of K step kt+2 go out one per two MFMAs, half
-//    after that barrier and half in the first k16 step of K step kt+1, each
-//    with at least two k16 steps to land before the barrier that needs it.
-// The plain and q/k/v epilogues take the four-wave form; the gated epilogue
-// the eight-wave form, where its norm and partial rotation fit without spills.
-// Every epilogue stages the finished tile in LDS (the ring is idle by then) and
-// stores whole rows.
+//    take a third less.
+// In both the tiles go HBM -> LDS directly (global_load_lds_dwordx4, no staging
+// registers) into a two-stage ring; the barrier that publishes K step kt+1
+// sits before the last k16 step of K step kt, whose fragments are already in
+// registers, and the copies of K step kt+2 go out one per two MFMAs, half after
+// that barrier and half in the first k16 step of K step kt+1, each with at
+// least two k16 steps to land before the barrier that needs it.
+// The plain epilogue takes the four-wave form, the q/k/v epilogues the
+// eight-wave form.  Every epilogue stages the finished tile in LDS (the ring is
+// idle by then) and stores whole rows.
 // Either way a wave owns exactly one head block of 128 columns, and in the
 // transposed accumulator a lane owns ONE token (lane % 32) and 64 of the
 // block's 128 columns (the other 64 sit in lane ^ 32), and columns c and
@@ -183,10 +181,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
   constexpr int kReads = 4 + kTB;  // fragment reads per k16 step
 
   if constexpr (WAVES == 8) {
-    // Staging: wave w moves blocks 4w .. 4w+3 of both tiles; lane l carries
-    // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- so its LDS
-    // address inside a block is 16 l.  Rows past the matrix repeat its last row
-    // (their results are never stored).
+    // Copies: wave w fills blocks 4w .. 4w+3 of both tiles; lane l carries
+    // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- its LDS address
+    // inside the block is 16 l.  Rows past the matrix repeat its last row
+    // (their results are never stored).  The schedule is the four-wave form's:
+    // the barrier that publishes K step kt+1 sits before K step kt's last k16
+    // step, and K step kt+2's 8 copies per lane go out one per two MFMAs, half
+    // after that barrier and half in K step kt+1's first k16 step.
     uint32_t xo[4], wo[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -194,58 +195,75 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_gemm(GemmArgs a) {
       xo[m] = (uint32_t)(min(r, last_x) * xrow) + (lane & 7) * 16;
       wo[m] = (uint32_t)(min(r, last_w) * wrow) + (lane & 7) * 16;
     }
-    u32x4 stg[8];  // one K step in flight: x blocks (0..3), then W blocks (4..7)
-    auto gload = [&](int kt, int m) __attribute__((always_inline)) {
-      const char* p = (m < 4 ? xbase + xo[m] : wbase + wo[m - 4]) + (int64_t)kt * kBK * 2;
-      stg[m] = *reinterpret_cast<const u32x4*>(p);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    // copy m (0 .. 7) of K step kt: x block 4w + m (m < 4), then W block 4w + m - 4
+    auto copy = [&](int kt, int m) __attribute__((always_inline)) {
+      const uint32_t dst = lds0 + (kt & 1) * kStageBytes + (m < 4 ? 0 : kTile) + (wu * 4 + (m & 3)) * kBlk;
+      const char* src = (m < 4 ? xbase : wbase) + (int64_t)kt * kBK * 2;
+      load_lds16_async(dst, src, m < 4 ? xo[m] : wo[m - 4]);
     };
-    auto lwrite = [&](int kt, int m) __attribute__((always_inline)) {
-      lds_u8* base = lds + (kt & 1) * kStageBytes + (m < 4 ? 0 : kTile) + (w * 4 + (m & 3)) * kBlk + lane * 16;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base) = stg[m];
+    // K step 0 and the first half of K step 1; wait for step 0.
+#pragma unroll
+    for (int m = 0; m < 8; ++m) copy(0, m);
+    if (nk > 1) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) copy(1, m);
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kReads; ++r) read(0, 0, r);
+    // The 8 MFMAs of k16 step s, each followed by fn(i); sched_barrier keeps
+    // the order, so every read and copy has the MFMAs after it to land; the two
+    // waves of a SIMD interleave their streams.
+    auto mfmas = [&](int s, auto fn) __attribute__((always_inline)) {
+      const int buf = s & 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int jc = i >> 1, it = i & 1;
+        acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][jc], xf[buf][it], acc[jc][it], 0, 0, 0);
+        fn(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
-    // K step 0 into LDS stage 0; K step 1 into the staging registers.
-#pragma unroll
-    for (int m = 0; m < 8; ++m) gload(0, m);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) lwrite(0, m);
-    if (nk > 1)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) gload(1, m);
-    // One K step: kMore / kMore2 say whether K steps kt+1 / kt+2 exist
+    // One K step; kMore / kMore2 say whether K steps kt+1 / kt+2 exist
     // (compile-time in the steady state, so the MFMA stream has no branches).
     auto step = [&](int kt, auto more_tag, auto more2_tag) __attribute__((always_inline)) {
       constexpr bool kMore = decltype(more_tag)::value, kMore2 = decltype(more2_tag)::value;
-      // Step kt is in LDS (every wave's writes done and published); the other
-      // stage, which held step kt-1, is free for step kt+1.
-      __syncthreads();
+      // k16 steps 0..2; the 6 fragments of step s+1 are read during step s, and
+      // k16 step 0 sends the second half of K step kt+1's copies.
+      mfmas(0, [&](int i) __attribute__((always_inline)) {
+        if (i < kReads) read(kt, 1, i);
+        if constexpr (kMore)
+          if ((i & 1) == 0) copy(kt + 1, 4 + (i >> 1));
+      });
 #pragma unroll
-      for (int r = 0; r < kReads; ++r) read(kt, 0, r);
-      // Four k16 steps of 8 MFMAs.  The 6 fragments of step s+1 are read during
-      // step s; after every fourth MFMA one staged block of K step kt+1 goes to
-      // LDS and its register is refilled with the same block of K step kt+2, so
-      // each load has a whole K step to land.  sched_barrier keeps that order;
-      // the two waves of a SIMD interleave their streams.
-#pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
-        const int buf = s & 1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int jc = i >> 1, it = i & 1;
-          acc[jc][it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][jc], xf[buf][it], acc[jc][it], 0, 0, 0);
-          if (s + 1 < kBK / 16 && i < kReads) read(kt, s + 1, i);
-          if ((i & 3) == 3) {
-            const int m = 2 * s + (i >> 2);
-            if constexpr (kMore) lwrite(kt + 1, m);
-            if constexpr (kMore2) gload(kt + 2, m);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int s = 1; s < 3; ++s)
+        mfmas(s, [&](int i) __attribute__((always_inline)) {
+          if (i < kReads) read(kt, s + 1, i);
+        });
+      if constexpr (kMore) {
+        // This wave's copies of K step kt+1 have landed; the barrier publishes
+        // everyone's and (its fragment reads done) frees stage kt & 1.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
       }
+      // k16 step 3 from registers; meanwhile the first fragments of K step
+      // kt+1 and the first half of K step kt+2's copies into the freed stage.
+      mfmas(3, [&](int i) __attribute__((always_inline)) {
+        if constexpr (kMore)
+          if (i < kReads) read(kt + 1, 0, i);
+        if constexpr (kMore2)
+          if ((i & 1) == 0) copy(kt + 2, i >> 1);
+      });
     };
     int kt = 0;
     for (; kt + 2 < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
     if (kt + 1 < nk) step(kt++, std::true_type{}, std::false_type{});
-    if (kt < nk) step(kt, std::false_type{}, std::false_type{});
+    step(kt, std::false_type{}, std::false_type{});
   } else {
     // Copies: wave w fills blocks 8w .. 8w+7 of both tiles; lane l carries
     // slot l / 8 (row blk + 32 (l / 8)), 16-byte chunk l % 8 -- its LDS
@@ -621,15 +639,15 @@ hipError_t launch_w(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The four-wave form for the plain and q/k/v epilogues, at every width (with
-// the tile staged through LDS on its way out it measured 6-11% faster than the
-// eight-wave form from 256 to 3072 columns, and faster above).  The gated
-// epilogue takes the eight-wave form: with 4 x 4 accumulators live its norm and
-// partial rotation spill.
+// The plain epilogue takes the four-wave form (1-4% ahead of the eight-wave
+// form at every width measured); the q/k/v epilogues take the eight-wave form,
+// whose second wave per SIMD covers the norm, rotation and position lookups
+// (1% ahead on the Qwen3-8B projection), and where the gated epilogue fits
+// without spills.
 template <int EPI>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  if constexpr (EPI >= kGemmQkvGated) return launch_w<EPI, 8>(a, st);
-  else return launch_w<EPI, 4>(a, st);
+  if constexpr (EPI == kGemmPlain) return launch_w<EPI, 4>(a, st);
+  else return launch_w<EPI, 8>(a, st);
 }
 
 }  // namespace

@@ -45,7 +45,7 @@ def linear_bound(x, w, k):
 # 256 x 256 tiles: 4 x 8 blocks in 4 x 2 regions (one and two block columns per
 # region), and 8 x 4 blocks in 8 x 1 regions with the per-XCD column-block
 # rotation (one, three and six block columns).  The eight-wave form serves the
-# gated q/k/v epilogue, tested with the gated sublayer.
+# q/k/v epilogues, tested with the sublayers.
 @pytest.mark.parametrize("m,n,k", [(1, 128, 64), (255, 384, 128), (257, 256, 1024), (1000, 640, 320),
                                    (4096, 1024, 4096), (1, 4096, 64), (257, 4224, 128), (1000, 4096, 320),
                                    (300, 6144, 4096), (4096, 4096, 64), (4096, 8192, 64), (16384, 1024, 64),
